@@ -1,0 +1,266 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) sparse-attention decode library.
+ *
+ * One step of DeepSeek native / DeepSeek sparse attention (NSA / DSA) per
+ * query row:
+ *   indexer logits -> length-masked top-k -> page-table transform ->
+ *   MLA attention over the selected KV slots of a shared 576-wide latent.
+ *
+ * Source pages cited below, by title:
+ *   [nsa-fork]  "nsa_backend.py (EngineX-Hygon sglang fork)"
+ *   [dsa-main]  "dsa_backend.py (sglang main)"
+ *   [nsa-diff]  "nsa_backend.py (sglang 0.5.3rc2 -> 0.5.4 diff)"
+ *
+ * Conventions shared by every call
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device; pointers named as host pointers to host memory.
+ *   - The caller owns every buffer. The library never allocates, frees, or
+ *     synchronises with the host; all work is enqueued on `stream` (a
+ *     hipStream_t; NULL is the default stream) and the call returns at once.
+ *   - Integer index tensors are int32. Strides are in elements.
+ *   - Index rows use -1 for unused entries, valid entries first.
+ *   - Every call returns NSA_OK (0) or a negative status. Arguments are
+ *     checked on the host before anything is launched; on error nothing is
+ *     launched and nsa_last_error() describes the problem. No call aborts.
+ *   - Device-side data the host cannot check (index values, page ids, slot
+ *     ids) is bounds-checked in the kernels: an out-of-range page id or slot
+ *     is treated as absent (see each call), never dereferenced.
+ */
+#ifndef NSA_H_
+#define NSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+#define NSA_OK 0
+#define NSA_ERR_INVALID_ARG (-1)  /* null pointer, negative size, bad stride */
+#define NSA_ERR_UNSUPPORTED (-2)  /* shape / dtype / page size not supported */
+#define NSA_ERR_WORKSPACE (-3)    /* workspace missing or too small */
+#define NSA_ERR_LAUNCH (-4)       /* the HIP runtime rejected a launch */
+
+/* ---- enums ---------------------------------------------------------------- */
+#define NSA_MODE_DECODE 0
+#define NSA_MODE_EXTEND 1
+#define NSA_MODE_TARGET_VERIFY 2
+
+#define NSA_DTYPE_FP32 0
+#define NSA_DTYPE_BF16 1
+#define NSA_DTYPE_FP8_E4M3 2  /* OCP e4m3fn */
+
+#define NSA_KV_BF16_576 0     /* latent row = 576 bf16 (1152 bytes) */
+#define NSA_KV_FP8_656 1      /* latent row = 656 bytes, see quantize below */
+
+#define NSA_PAGE_SIZE 64
+#define NSA_D_QK 576
+#define NSA_D_V 512
+
+/* Thread-local description of the last error returned on this thread
+ * ("" when the last call succeeded). The string stays valid until the next
+ * call on the same thread. */
+const char* nsa_last_error(void);
+
+/* Library version as an integer (major*10000 + minor*100 + patch). */
+int nsa_version(void);
+
+/* ---- a0: per-forward metadata ------------------------------------------------
+ * Defined by [nsa-fork] NSAMetadata, compute_cu_seqlens,
+ * _transform_table_1_to_real and NativeSparseAttnBackend.init_forward_metadata;
+ * [dsa-main] DeepseekSparseAttnBackend.init_forward_metadata (decode,
+ * target-verify and extend branches) and _cal_indexer_k_start_end (per-token
+ * batch index); [nsa-diff] target-verify metadata.
+ *
+ * Inputs (device, int32):
+ *   seq_lens[bs]          KV length per request (extend: including the new
+ *                         tokens; target-verify: excluding the drafts).
+ *   extend_lens[bs]       new tokens per request (EXTEND only, else NULL).
+ *   req_to_token          [pool_rows, rtt_stride] token -> physical slot.
+ *   req_pool_indices[bs]  each request's row of req_to_token.
+ * Host scalars:
+ *   mode                  NSA_MODE_*.
+ *   draft_token_num       draft tokens per request (TARGET_VERIFY, else 0).
+ *   topk                  selection size (clip for nsa_cache_seqlens).
+ *   page_size             must be 64.
+ *   max_seqlen_k          host bound >= every cache seqlen; sizes the tables.
+ *   num_q_rows            T: bs (decode), bs*draft (verify), sum of
+ *                         extend_lens (extend). Rows past T are never written.
+ * Outputs (device, int32, caller-allocated):
+ *   cache_seqlens[bs]         seq_lens (+ draft_token_num in verify).
+ *   cu_seqlens_k[bs+1]        [0, cumsum(cache_seqlens)].
+ *   cu_seqlens_q              decode and verify: [T+1] = arange(T+1) (every
+ *                             verify draft token is its own query row);
+ *                             extend: [bs+1] = [0, cumsum(extend_lens)].
+ *   seqlens_expanded[T]       visible KV length of each query row: decode =
+ *                             cache_seqlens; verify/extend: kv_len - q_len + 1
+ *                             ... kv_len per request.
+ *   nsa_cache_seqlens[T]      min(seqlens_expanded, topk).
+ *   nsa_cu_seqlens_k[T+1]     [0, cumsum(nsa_cache_seqlens)].
+ *   nsa_cu_seqlens_q[T+1]     arange(T+1).
+ *   real_page_table           [bs, rpt_stride], columns
+ *                             p < ceil(max_seqlen_k/64) written with
+ *                             req_to_token[row, 64 p] >> 6 (one row per
+ *                             request; the pages repeat it per draft token).
+ *   token_to_req[T]           request of each query row.
+ *   page_table_1              optional [bs, pt1_stride] copy of
+ *                             req_to_token[row, :max_seqlen_k]; NULL to skip
+ *                             (the wide table the DSA page drops in its fused
+ *                             decode graphs).
+ * Host must ensure rtt_stride >= max_seqlen_k, pt1_stride >= max_seqlen_k
+ * and rpt_stride >= ceil(max_seqlen_k/64); req_to_token must have at least
+ * max_seqlen_k readable columns in every row named by req_pool_indices.
+ */
+int nsa_build_metadata(int mode, int bs, int draft_token_num, int topk,
+                       int page_size, const int32_t* seq_lens,
+                       const int32_t* extend_lens, const int32_t* req_to_token,
+                       int64_t rtt_stride, const int32_t* req_pool_indices,
+                       int max_seqlen_k, int num_q_rows,
+                       int32_t* cache_seqlens, int32_t* cu_seqlens_k,
+                       int32_t* cu_seqlens_q, int32_t* seqlens_expanded,
+                       int32_t* nsa_cache_seqlens, int32_t* nsa_cu_seqlens_k,
+                       int32_t* nsa_cu_seqlens_q, int32_t* real_page_table,
+                       int64_t rpt_stride, int32_t* token_to_req,
+                       int32_t* page_table_1, int64_t pt1_stride,
+                       void* stream);
+
+/* ---- a1: indexer logits ("paged MQA logits") -----------------------------------
+ * The indexer reads the index-key cache through the 64-token page table
+ * ([nsa-fork] NSAIndexerMetadata.get_page_table_64) for the row's expanded
+ * seqlen ([dsa-main] _to_2d_context_lens: one context length per row).
+ * Scoring formula (the indexer itself is not on the pages; reading adopted):
+ *   logits[t, s] = kscale[s] * sum_h weights[t, h] * max(0, q[t,h,:] . k[s,:])
+ * for s < min(seqlens_expanded[t], max_seqlen_k). Positions at or past that
+ * length are NOT written.
+ *
+ *   q                [T, Hi, Di] row-major; fp8 e4m3 codes (q_dtype
+ *                    NSA_DTYPE_FP8_E4M3) or fp32 (NSA_DTYPE_FP32). Any
+ *                    query-side scale is folded into weights by the caller.
+ *   weights          [T, Hi] fp32.
+ *   k_index_cache    [num_pages] pages of 64 tokens; page bytes =
+ *                    64*Di*elem (keys, row-major [64][Di]) + 64*4 (fp32
+ *                    per-token scales). k_dtype must equal q_dtype.
+ *   real_page_table  [*, rpt_stride] page ids per request; a page id outside
+ *                    [0, num_pages) yields -inf logits for its 64 positions.
+ *   token_to_req[T], seqlens_expanded[T]  from nsa_build_metadata.
+ *   logits           [T, logits_stride] fp32, logits_stride >= max_seqlen_k.
+ * Supported: (fp8, Hi = 64, Di = 128) on the MFMA path; (fp32, Hi <= 64,
+ * Di <= 128, Di % 4 == 0). page_size must be 64.
+ */
+int nsa_indexer_logits(const void* q, int q_dtype, const float* weights,
+                       const void* k_index_cache, int k_dtype,
+                       int64_t num_pages, const int32_t* real_page_table,
+                       int64_t rpt_stride, const int32_t* token_to_req,
+                       const int32_t* seqlens_expanded, int T, int Hi, int Di,
+                       int page_size, int max_seqlen_k, float* logits,
+                       int64_t logits_stride, void* stream);
+
+/* ---- a2 (+a3 fused): length-masked top-k -----------------------------------------
+ * [nsa-fork] NSAIndexerMetadata.topk_transform: fast_topk_v2(logits,
+ * lengths, topk) returns logical positions; fast_topk_transform_fused(...)
+ * returns physical slots through the page table. Field comment of
+ * nsa_cache_seqlens_int32: the effective length is clipped to topk.
+ *
+ * Row t keeps n = min(lengths[t], max_seqlen_k): if n <= topk every position
+ * 0..n-1, else the topk positions with the largest logits[t, 0:n]. The row of
+ * `out` holds the kept entries in ascending position order, then -1. Ties at
+ * the threshold are broken by ascending position. NaN logits rank lowest.
+ *   table == NULL    out holds logical positions.
+ *   table != NULL    out holds physical slots: table is the compact page
+ *                    table [*, table_stride] (real_page_table) and
+ *                    slot = table[token_to_req[t], i >> 6] * 64 + (i & 63).
+ *   workspace        device scratch of nsa_topk_workspace_size() bytes (may
+ *                    be NULL when that size is 0).
+ */
+int nsa_topk_workspace_size(int T, int max_seqlen_k, int topk, size_t* bytes);
+int nsa_topk_transform(const float* logits, int64_t logits_stride,
+                       const int32_t* lengths, int T, int topk,
+                       int max_seqlen_k, const int32_t* table,
+                       int64_t table_stride, const int32_t* token_to_req,
+                       int page_size, int32_t* out, int64_t out_stride,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- a3: page-table transform ---------------------------------------------------
+ * [nsa-fork] forward_decode / forward_extend:
+ * transform_index_page_table_decode / _prefill(page_table_1, topk_indices,
+ * page_size=1). out[t, j] = -1 if idx < 0, else the physical slot of logical
+ * position idx of request token_to_req[t]: page_table_1[r, idx] (wide form)
+ * or real_page_table[r, idx >> 6] * 64 + (idx & 63) (compact form). Exactly
+ * one of page_table_1 / real_page_table must be non-NULL. Indices at or past
+ * the table width give -1.
+ */
+int nsa_page_table_transform(const int32_t* topk_indices, int64_t in_stride,
+                             int T, int topk, const int32_t* page_table_1,
+                             int64_t pt1_stride, int64_t pt1_width,
+                             const int32_t* real_page_table,
+                             int64_t rpt_stride, int64_t rpt_width,
+                             int page_size, const int32_t* token_to_req,
+                             int32_t* out, int64_t out_stride, void* stream);
+
+/* ---- a4 / a5: sparse MLA over selected slots ------------------------------------
+ * [nsa-fork] _forward_fa3 (semantics: score = q_rope.k_rope + q_nope.c_kv,
+ * value = c_kv, over the first nsa_cache_seqlens[t] entries of the
+ * transformed table), _forward_flashmla_decode / [dsa-main]
+ * _forward_flashmla_kv (q [T, H, 576], cache viewed as [pages, 64, 1, dim],
+ * indices width == topk, returns o and lse), _forward_flashmla_sparse.
+ *
+ *   q            bf16, element (t, h, d) at q[t*q_tok_stride + h*q_head_stride
+ *                + d], d < 576 (512 no-rope then 64 rope).
+ *   kv_cache     [num_slots] rows: NSA_KV_BF16_576 (576 bf16) or
+ *                NSA_KV_FP8_656 (the quantize_k_cache layout).
+ *   indices      [T, idx_stride] int32 physical slots, -1 = unused; a slot
+ *                outside [0, num_slots) counts as unused.
+ *   nsa_cache_seqlens  optional [T]: only the first nsa_cache_seqlens[t]
+ *                entries of row t are read (NULL: all topk entries).
+ *   out          [T, H, 512] bf16, contiguous.
+ *   lse          optional [T, H] fp32 natural-log log-sum-exp of the scaled
+ *                scores (-inf for a row with no valid slot; out = 0 there).
+ *   workspace    device scratch >= nsa_sparse_mla_workspace_size(...) bytes.
+ * Supported: H in {16, 32, ..., 128}, d_qk = 576, d_v = 512, topk <= 8192,
+ * q pointer 16-byte aligned and strides multiples of 8 elements.
+ * The result is bit-reproducible (fixed-order combine of KV splits).
+ * _decode plans KV splits for small T (decode, verify rows); _extend for
+ * many rows (chunked prefill). Both compute the same function.
+ */
+int nsa_sparse_mla_workspace_size(int T, int H, int topk, int d_v,
+                                  size_t* bytes);
+int nsa_sparse_mla_decode(const void* q, int64_t q_tok_stride,
+                          int64_t q_head_stride, const void* kv_cache,
+                          int kv_dtype, int64_t num_slots,
+                          const int32_t* indices, int64_t idx_stride,
+                          const int32_t* nsa_cache_seqlens, int T, int H,
+                          int topk, int d_qk, int d_v, float sm_scale,
+                          void* out, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream);
+int nsa_sparse_mla_extend(const void* q, int64_t q_tok_stride,
+                          int64_t q_head_stride, const void* kv_cache,
+                          int kv_dtype, int64_t num_slots,
+                          const int32_t* indices, int64_t idx_stride,
+                          const int32_t* nsa_cache_seqlens, int T, int H,
+                          int topk, int d_qk, int d_v, float sm_scale,
+                          void* out, float* lse, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* ---- a6: fp8 block-scaled latent cache --------------------------------------------
+ * [nsa-fork] _forward_flashmla_decode and [dsa-main] _forward_flashmla_kv
+ * call quantize_k_cache(kv_cache) to produce the fp8 cache the decode kernel
+ * reads (page size 64). Layout (a reading; the body is not on the pages),
+ * one 656-byte row per slot:
+ *   [0, 512)    e4m3fn codes of the 512 no-rope values, 4 blocks of 128
+ *   [512, 528)  4 fp32 block scales, scale_b = amax_b / 448 (1 if amax_b = 0)
+ *   [528, 656)  64 rope values, bf16, copied
+ * code = round-to-nearest-even, saturating e4m3fn of (x / scale_b), the
+ * division correctly rounded in fp32.
+ *   kv_bf16   [num_slots, in_stride] bf16, first 576 elements used.
+ *   out       [num_slots, 656] bytes.
+ */
+int nsa_quantize_k_cache(const void* kv_bf16, int64_t num_slots,
+                         int64_t in_stride, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H_ */

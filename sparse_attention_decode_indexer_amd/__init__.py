@@ -1,0 +1,225 @@
+"""MI355X (gfx950) sparse-attention decode step: Python binding of libnsa.so.
+
+Every step of the path runs in the library's HIP kernels; this module only
+marshals arguments: it checks torch tensors (device, dtype, contiguity),
+allocates outputs with torch when none are given, and passes raw pointers and
+the current HIP stream to the C ABI declared in include/nsa.h. There is no
+fallback: if the library is missing, the calls raise.
+
+Names follow the C entry points. Constants mirror nsa.h.
+"""
+
+import ctypes
+
+import torch
+
+from ._lib import NsaError, call, load  # noqa: F401
+
+MODE_DECODE, MODE_EXTEND, MODE_TARGET_VERIFY = 0, 1, 2
+DTYPE_FP32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+KV_BF16_576, KV_FP8_656 = 0, 1
+PAGE_SIZE, D_QK, D_V = 64, 576, 512
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t, name, dtype=None, ndim=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def nsa_build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
+                       max_seqlen_k, num_q_rows, extend_lens=None,
+                       draft_token_num=0, page_size=PAGE_SIZE,
+                       want_page_table_1=False):
+    """Per-forward metadata (one kernel launch). Returns a dict of int32
+    device tensors named as in nsa.h."""
+    i32 = torch.int32
+    _check(seq_lens, "seq_lens", i32, 1)
+    _check(req_to_token, "req_to_token", i32, 2)
+    _check(req_pool_indices, "req_pool_indices", i32, 1)
+    if extend_lens is not None:
+        _check(extend_lens, "extend_lens", i32, 1)
+    bs = seq_lens.numel()
+    T = int(num_q_rows)
+    dev = seq_lens.device
+    ncols = (max_seqlen_k + PAGE_SIZE - 1) // PAGE_SIZE
+    nq = bs + 1 if mode == MODE_EXTEND else T + 1
+    out = dict(
+        cache_seqlens=torch.empty(bs, dtype=i32, device=dev),
+        cu_seqlens_k=torch.empty(bs + 1, dtype=i32, device=dev),
+        cu_seqlens_q=torch.empty(nq, dtype=i32, device=dev),
+        seqlens_expanded=torch.empty(T, dtype=i32, device=dev),
+        nsa_cache_seqlens=torch.empty(T, dtype=i32, device=dev),
+        nsa_cu_seqlens_k=torch.empty(T + 1, dtype=i32, device=dev),
+        nsa_cu_seqlens_q=torch.empty(T + 1, dtype=i32, device=dev),
+        real_page_table=torch.empty(bs, max(ncols, 1), dtype=i32, device=dev),
+        token_to_req=torch.empty(T, dtype=i32, device=dev),
+    )
+    pt1 = (torch.empty(bs, max(max_seqlen_k, 1), dtype=i32, device=dev)
+           if want_page_table_1 else None)
+    call("nsa_build_metadata", mode, bs, draft_token_num, topk, page_size,
+         _ptr(seq_lens), _ptr(extend_lens), _ptr(req_to_token),
+         req_to_token.stride(0), _ptr(req_pool_indices), max_seqlen_k, T,
+         _ptr(out["cache_seqlens"]), _ptr(out["cu_seqlens_k"]),
+         _ptr(out["cu_seqlens_q"]), _ptr(out["seqlens_expanded"]),
+         _ptr(out["nsa_cache_seqlens"]), _ptr(out["nsa_cu_seqlens_k"]),
+         _ptr(out["nsa_cu_seqlens_q"]), _ptr(out["real_page_table"]),
+         out["real_page_table"].stride(0), _ptr(out["token_to_req"]),
+         _ptr(pt1), pt1.stride(0) if pt1 is not None else 0, _stream())
+    if pt1 is not None:
+        out["page_table_1"] = pt1
+    return out
+
+
+def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
+                       seqlens_expanded, max_seqlen_k, logits=None,
+                       dtype=DTYPE_FP8_E4M3):
+    """Indexer logits [T, >= max_seqlen_k] fp32 (positions past each row's
+    length are left unwritten). ``q``: [T, Hi, Di] uint8 fp8 codes (dtype
+    DTYPE_FP8_E4M3) or float32 (DTYPE_FP32)."""
+    _check(q, "q", torch.uint8 if dtype == DTYPE_FP8_E4M3 else torch.float32, 3)
+    _check(weights, "weights", torch.float32, 2)
+    _check(index_cache, "index_cache", torch.uint8, 2)
+    _check(real_page_table, "real_page_table", torch.int32, 2)
+    _check(token_to_req, "token_to_req", torch.int32, 1)
+    _check(seqlens_expanded, "seqlens_expanded", torch.int32, 1)
+    T, Hi, Di = q.shape
+    if logits is None:
+        logits = torch.empty(T, max(max_seqlen_k, 1), dtype=torch.float32,
+                             device=q.device)
+    _check(logits, "logits", torch.float32, 2, contiguous=False)
+    call("nsa_indexer_logits", _ptr(q), dtype, _ptr(weights), _ptr(index_cache),
+         dtype, index_cache.shape[0], _ptr(real_page_table),
+         real_page_table.stride(0), _ptr(token_to_req), _ptr(seqlens_expanded),
+         T, Hi, Di, PAGE_SIZE, max_seqlen_k, _ptr(logits), logits.stride(0),
+         _stream())
+    return logits
+
+
+def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
+                       token_to_req=None, out=None):
+    """Top-k positions per row (ascending position order, -1 padded), or
+    physical slots when ``table`` (the compact page table) is given."""
+    _check(lengths, "lengths", torch.int32, 1)
+    T = lengths.numel()
+    if logits is not None:
+        _check(logits, "logits", torch.float32, 2, contiguous=False)
+    if table is not None:
+        _check(table, "table", torch.int32, 2)
+        _check(token_to_req, "token_to_req", torch.int32, 1)
+    if out is None:
+        out = torch.empty(T, topk, dtype=torch.int32, device=lengths.device)
+    _check(out, "out", torch.int32, 2, contiguous=False)
+    ws = ctypes.c_size_t(0)
+    call("nsa_topk_workspace_size", T, max_seqlen_k, topk, ctypes.byref(ws))
+    work = (torch.empty(ws.value, dtype=torch.uint8, device=lengths.device)
+            if ws.value else None)
+    call("nsa_topk_transform", _ptr(logits),
+         logits.stride(0) if logits is not None else 0, _ptr(lengths), T, topk,
+         max_seqlen_k, _ptr(table), table.stride(0) if table is not None else 0,
+         _ptr(token_to_req), PAGE_SIZE, _ptr(out), out.stride(0), _ptr(work),
+         ws.value, _stream())
+    return out
+
+
+def nsa_page_table_transform(topk_indices, token_to_req, page_table_1=None,
+                             real_page_table=None, out=None):
+    """Logical positions -> physical slots (-1 kept). Give exactly one table."""
+    _check(topk_indices, "topk_indices", torch.int32, 2, contiguous=False)
+    _check(token_to_req, "token_to_req", torch.int32, 1)
+    T, K = topk_indices.shape
+    if out is None:
+        out = torch.empty(T, K, dtype=torch.int32, device=topk_indices.device)
+    pt1_stride = pt1_width = rpt_stride = rpt_width = 0
+    if page_table_1 is not None:
+        _check(page_table_1, "page_table_1", torch.int32, 2, contiguous=False)
+        pt1_stride, pt1_width = page_table_1.stride(0), page_table_1.shape[1]
+    if real_page_table is not None:
+        _check(real_page_table, "real_page_table", torch.int32, 2, contiguous=False)
+        rpt_stride, rpt_width = real_page_table.stride(0), real_page_table.shape[1]
+    call("nsa_page_table_transform", _ptr(topk_indices), topk_indices.stride(0),
+         T, K, _ptr(page_table_1), pt1_stride, pt1_width, _ptr(real_page_table),
+         rpt_stride, rpt_width, PAGE_SIZE, _ptr(token_to_req), _ptr(out),
+         out.stride(0), _stream())
+    return out
+
+
+def sparse_mla_workspace_size(T, H, topk):
+    ws = ctypes.c_size_t(0)
+    call("nsa_sparse_mla_workspace_size", T, H, topk, D_V, ctypes.byref(ws))
+    return ws.value
+
+
+def _sparse_mla(name, q, kv_cache, kv_dtype, indices, sm_scale,
+                nsa_cache_seqlens, out, lse, workspace, want_lse):
+    _check(q, "q", torch.bfloat16, 3, contiguous=False)
+    if q.stride(2) != 1:
+        raise ValueError("q must be contiguous in its last dimension")
+    T, H, dqk = q.shape
+    if kv_dtype == KV_BF16_576:
+        _check(kv_cache, "kv_cache", torch.bfloat16, 2)
+    else:
+        _check(kv_cache, "kv_cache", torch.uint8, 2)
+    _check(indices, "indices", torch.int32, 2, contiguous=False)
+    if nsa_cache_seqlens is not None:
+        _check(nsa_cache_seqlens, "nsa_cache_seqlens", torch.int32, 1)
+    topk = indices.shape[1]
+    if out is None:
+        out = torch.empty(T, H, D_V, dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(T, H, dtype=torch.float32, device=q.device)
+    need = sparse_mla_workspace_size(T, H, topk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    call(name, _ptr(q), q.stride(0), q.stride(1), _ptr(kv_cache), kv_dtype,
+         kv_cache.shape[0], _ptr(indices), indices.stride(0),
+         _ptr(nsa_cache_seqlens), T, H, topk, dqk, D_V, float(sm_scale),
+         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream())
+    return out, lse
+
+
+def nsa_sparse_mla_decode(q, kv_cache, kv_dtype, indices, sm_scale,
+                          nsa_cache_seqlens=None, out=None, lse=None,
+                          workspace=None, want_lse=True):
+    """Sparse MLA over selected slots (decode / verify rows): returns
+    (out [T, H, 512] bf16, lse [T, H] fp32 or None)."""
+    return _sparse_mla("nsa_sparse_mla_decode", q, kv_cache, kv_dtype, indices,
+                       sm_scale, nsa_cache_seqlens, out, lse, workspace, want_lse)
+
+
+def nsa_sparse_mla_extend(q, kv_cache, kv_dtype, indices, sm_scale,
+                          nsa_cache_seqlens=None, out=None, lse=None,
+                          workspace=None, want_lse=True):
+    """Sparse MLA for many query rows (chunked extend)."""
+    return _sparse_mla("nsa_sparse_mla_extend", q, kv_cache, kv_dtype, indices,
+                       sm_scale, nsa_cache_seqlens, out, lse, workspace, want_lse)
+
+
+def nsa_quantize_k_cache(kv_bf16, out=None):
+    """bf16 latent cache [slots, >=576] -> fp8 block-scaled [slots, 656] uint8."""
+    _check(kv_bf16, "kv_bf16", torch.bfloat16, 2, contiguous=False)
+    if kv_bf16.stride(1) != 1:
+        raise ValueError("kv_bf16 rows must be contiguous")
+    n = kv_bf16.shape[0]
+    if out is None:
+        out = torch.empty(n, 656, dtype=torch.uint8, device=kv_bf16.device)
+    _check(out, "out", torch.uint8, 2)
+    call("nsa_quantize_k_cache", _ptr(kv_bf16), n, kv_bf16.stride(0), _ptr(out),
+         _stream())
+    return out

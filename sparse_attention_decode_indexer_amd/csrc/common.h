@@ -1,0 +1,68 @@
+// Internal helpers shared by the library's translation units: status and
+// last-error handling, host-side argument checks, small device utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "nsa.h"
+
+namespace nsa {
+
+// Records a formatted message as this thread's last error and returns code.
+int set_error(int code, const char* fmt, ...);
+// Clears this thread's last error and returns NSA_OK.
+int ok();
+
+// Translates the result of the launch just issued into a status.
+inline int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_error(NSA_ERR_LAUNCH, "%s: launch failed: %s", what,
+                     hipGetErrorString(e));
+  return ok();
+}
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+}  // namespace nsa
+
+#define NSA_REQUIRE(cond, code, ...)              \
+  do {                                            \
+    if (!(cond)) return nsa::set_error(code, __VA_ARGS__); \
+  } while (0)
+
+// ---- device helpers --------------------------------------------------------
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Packs two floats into one dword of two bfloat16 (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}

@@ -1,0 +1,267 @@
+// a1: indexer logits ("paged MQA logits") over the 64-token paged index-key
+// cache.
+//
+// The pages feed the indexer the compact 64-token page table
+// ("nsa_backend.py (EngineX-Hygon sglang fork)",
+// NSAIndexerMetadata.get_page_table_64) and one context length per query row
+// ("dsa_backend.py (sglang main)", _to_2d_context_lens). The scoring formula
+// is the reading stated in nsa.h:
+//   logits[t, s] = kscale[s] * sum_h w[t, h] * relu(q[t, h, :] . k[s, :]).
+//
+// fp8 path (Hi = 64 heads, Di = 128), MI355X design:
+//   * one block of 4 waves per (row, chunk of 32 pages); wave w takes pages
+//     w, w+4, ... of the chunk, so a wave always works on a whole page
+//     (64 tokens = 8 KB of keys + 256 B of scales, contiguous);
+//   * v_mfma_f32_16x16x128_f8f6f4 with A = 16 heads x 128 dims of q (held in
+//     registers for the whole block) and B = 128 dims x 16 tokens of keys, so
+//     the dot products over all 128 dims take one instruction and the output
+//     holds 4 heads x 1 token per lane;
+//   * ReLU and the head weights are applied in registers; the 64-head sum is
+//     16 in-lane FMAs plus a 3-shuffle transpose-reduce that leaves token
+//     lane in lane `lane`, so each page is stored as 64 consecutive floats;
+//   * keys are loaded straight from HBM with 16-byte loads (each instruction
+//     reads 64 contiguous bytes of 16 key rows), the next page's loads are
+//     issued before the current page's MFMAs.
+// The contraction dimension is split over lanes identically for q and for
+// the keys (each lane takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of a
+// 128-byte row, g = lane / 16), so the dot products do not depend on the
+// hardware's order of the contraction within an instruction.
+#include "common.h"
+
+namespace {
+
+constexpr int kPage = 64;
+constexpr int kHeads = 64;
+constexpr int kDim = 128;
+constexpr int kPageBytesFp8 = kPage * kDim + kPage * 4;  // 8448
+constexpr int kWaves = 4;
+constexpr int kPagesPerBlock = 32;
+
+// Logical block id such that consecutive ids run on the same XCD (work
+// groups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ uint32_t xcd_logical_block(uint32_t bid, uint32_t n) {
+  const uint32_t q = n / 8, r = n % 8, x = bid % 8;
+  return x * q + (x < r ? x : r) + bid / 8;
+}
+
+struct PageKeys {
+  i32x8 k[4];  // 4 tiles of 16 tokens
+};
+
+__device__ __forceinline__ void load_page(PageKeys& pk, const uint8_t* base,
+                                          int c, int g) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint8_t* row = base + (j * 16 + c) * kDim;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + g * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 + g * 16);
+    pk.k[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+}
+
+__global__ void __launch_bounds__(256)
+indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
+                   const uint8_t* __restrict__ cache, int64_t num_pages,
+                   const int32_t* __restrict__ rpt, int64_t rpt_stride,
+                   const int32_t* __restrict__ t2r,
+                   const int32_t* __restrict__ seqlens, int max_seqlen_k,
+                   float* __restrict__ logits, int64_t logits_stride,
+                   int chunks_per_row) {
+  const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int64_t t = lb / chunks_per_row;
+  const int chunk = lb % chunks_per_row;
+  int L = seqlens[t];
+  L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
+  const int npages = (L + kPage - 1) / kPage;
+  const int p_begin = chunk * kPagesPerBlock;
+  if (p_begin >= npages) return;
+  const int p_end = min(p_begin + kPagesPerBlock, npages);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+
+  // A operands: q rows of heads ht*16 + c, the lane's two 16-byte pieces
+  const uint8_t* qrow = q + t * (kHeads * kDim);
+  i32x8 qa[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const uint8_t* hr = qrow + (ht * 16 + c) * kDim;
+    const uint4 lo = *reinterpret_cast<const uint4*>(hr + g * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(hr + 64 + g * 16);
+    qa[ht] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  // weights of the heads this lane's accumulators hold: ht*16 + 4g + r
+  float wr[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const float4 v = *reinterpret_cast<const float4*>(w + t * kHeads + ht * 16 + 4 * g);
+    wr[ht][0] = v.x; wr[ht][1] = v.y; wr[ht][2] = v.z; wr[ht][3] = v.w;
+  }
+
+  const int32_t* prow = rpt + (int64_t)t2r[t] * rpt_stride;
+  float* lrow = logits + t * logits_stride;
+
+  int p = p_begin + wave;
+  if (p >= p_end) return;
+  int page = __builtin_amdgcn_readfirstlane(prow[p]);
+  bool ok = page >= 0 && page < num_pages;
+  PageKeys cur;
+  if (ok) load_page(cur, cache + (int64_t)page * kPageBytesFp8, c, g);
+
+  while (true) {
+    const int pn = p + kWaves;
+    int page_n = 0;
+    bool ok_n = false;
+    PageKeys nxt;
+    if (pn < p_end) {
+      page_n = __builtin_amdgcn_readfirstlane(prow[pn]);
+      ok_n = page_n >= 0 && page_n < num_pages;
+      if (ok_n) load_page(nxt, cache + (int64_t)page_n * kPageBytesFp8, c, g);
+    }
+
+    float result = -INFINITY;
+    if (ok) {
+      const uint8_t* base = cache + (int64_t)page * kPageBytesFp8;
+      const float ks = *reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane);
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qa[ht], cur.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s = fmaf(wr[ht][r], fmaxf(acc[r], 0.0f), s);
+        }
+        v[j] = s;
+      }
+      // transpose-reduce over the 4 lane groups: group g keeps tile g
+      const bool b0 = g & 1, b1 = (g >> 1) & 1;
+      const float u0 = (b0 ? v[1] : v[0]) + __shfl_xor(b0 ? v[0] : v[1], 16);
+      const float u1 = (b0 ? v[3] : v[2]) + __shfl_xor(b0 ? v[2] : v[3], 16);
+      const float tot = (b1 ? u1 : u0) + __shfl_xor(b1 ? u0 : u1, 32);
+      result = tot * ks;  // token p*64 + lane
+    }
+    const int s = p * kPage + lane;
+    if (s < L) lrow[s] = result;
+
+    if (pn >= p_end) break;
+    p = pn;
+    page = page_n;
+    ok = ok_n;
+    cur = nxt;
+  }
+}
+
+// fp32 path (small head counts / dims): one thread per position.
+__global__ void __launch_bounds__(256)
+indexer_fp32_kernel(const float* __restrict__ q, const float* __restrict__ w,
+                    const uint8_t* __restrict__ cache, int64_t num_pages,
+                    const int32_t* __restrict__ rpt, int64_t rpt_stride,
+                    const int32_t* __restrict__ t2r,
+                    const int32_t* __restrict__ seqlens, int max_seqlen_k,
+                    float* __restrict__ logits, int64_t logits_stride, int Hi,
+                    int Di, int chunks_per_row) {
+  extern __shared__ float smem[];  // q row [Hi*Di] then w [Hi]
+  const int64_t t = blockIdx.x / chunks_per_row;
+  const int chunk = blockIdx.x % chunks_per_row;
+  int L = seqlens[t];
+  L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
+  const int s = chunk * 256 + threadIdx.x;
+  if (chunk * 256 >= L) return;
+  float* qs = smem;
+  float* ws = smem + Hi * Di;
+  for (int i = threadIdx.x; i < Hi * Di; i += 256) qs[i] = q[t * Hi * Di + i];
+  for (int i = threadIdx.x; i < Hi; i += 256) ws[i] = w[t * Hi + i];
+  __syncthreads();
+  if (s >= L) return;
+  const int page = rpt[(int64_t)t2r[t] * rpt_stride + s / kPage];
+  float out = -INFINITY;
+  if (page >= 0 && page < num_pages) {
+    const int64_t page_bytes = (int64_t)kPage * Di * 4 + kPage * 4;
+    const uint8_t* base = cache + page * page_bytes;
+    const float* k = reinterpret_cast<const float*>(base) + (s % kPage) * Di;
+    const float ks = reinterpret_cast<const float*>(base + (int64_t)kPage * Di * 4)[s % kPage];
+    float acc = 0.0f;
+    for (int h = 0; h < Hi; ++h) {
+      float d = 0.0f;
+      for (int e = 0; e < Di; ++e) d = fmaf(qs[h * Di + e], k[e], d);
+      acc = fmaf(ws[h], fmaxf(d, 0.0f), acc);
+    }
+    out = acc * ks;
+  }
+  logits[t * logits_stride + s] = out;
+}
+
+}  // namespace
+
+extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
+                                  const float* weights,
+                                  const void* k_index_cache, int k_dtype,
+                                  int64_t num_pages,
+                                  const int32_t* real_page_table,
+                                  int64_t rpt_stride,
+                                  const int32_t* token_to_req,
+                                  const int32_t* seqlens_expanded, int T,
+                                  int Hi, int Di, int page_size,
+                                  int max_seqlen_k, float* logits,
+                                  int64_t logits_stride, void* stream) {
+  const char* fn = "nsa_indexer_logits";
+  NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0 && num_pages >= 0,
+              NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(page_size == NSA_PAGE_SIZE, NSA_ERR_UNSUPPORTED,
+              "%s: page_size %d (only 64 is supported)", fn, page_size);
+  NSA_REQUIRE(q_dtype == k_dtype, NSA_ERR_UNSUPPORTED,
+              "%s: q and key dtypes must match", fn);
+  const bool fp8 = q_dtype == NSA_DTYPE_FP8_E4M3;
+  NSA_REQUIRE(fp8 || q_dtype == NSA_DTYPE_FP32, NSA_ERR_UNSUPPORTED,
+              "%s: dtype %d (fp8 e4m3 or fp32 only)", fn, q_dtype);
+  if (fp8)
+    NSA_REQUIRE(Hi == kHeads && Di == kDim, NSA_ERR_UNSUPPORTED,
+                "%s: fp8 path needs Hi = 64, Di = 128 (got %d, %d)", fn, Hi, Di);
+  else
+    NSA_REQUIRE(Hi >= 1 && Hi <= 64 && Di >= 4 && Di <= 128 && Di % 4 == 0,
+                NSA_ERR_UNSUPPORTED,
+                "%s: fp32 path needs 1 <= Hi <= 64, 4 <= Di <= 128, Di %% 4 == 0",
+                fn);
+  if (T == 0 || max_seqlen_k == 0) return nsa::ok();
+  NSA_REQUIRE(q && weights && k_index_cache && real_page_table && token_to_req &&
+                  seqlens_expanded && logits,
+              NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(logits_stride >= max_seqlen_k, NSA_ERR_INVALID_ARG,
+              "%s: logits_stride < max_seqlen_k", fn);
+  const int64_t ncols = (max_seqlen_k + kPage - 1) / kPage;
+  NSA_REQUIRE(rpt_stride >= ncols, NSA_ERR_INVALID_ARG,
+              "%s: rpt_stride < ceil(max_seqlen_k/64)", fn);
+  NSA_REQUIRE(nsa::aligned(q, 16) && nsa::aligned(weights, 16) &&
+                  nsa::aligned(k_index_cache, 16) && nsa::aligned(logits, 4),
+              NSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  if (fp8) {
+    const int chunks = (int)((ncols + kPagesPerBlock - 1) / kPagesPerBlock);
+    const int64_t blocks = (int64_t)T * chunks;
+    NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    hipLaunchKernelGGL(indexer_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       s, static_cast<const uint8_t*>(q), weights,
+                       static_cast<const uint8_t*>(k_index_cache), num_pages,
+                       real_page_table, rpt_stride, token_to_req,
+                       seqlens_expanded, max_seqlen_k, logits, logits_stride,
+                       chunks);
+  } else {
+    const int chunks = (max_seqlen_k + 255) / 256;
+    const int64_t blocks = (int64_t)T * chunks;
+    NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    const size_t shm = (size_t)(Hi * Di + Hi) * sizeof(float);
+    hipLaunchKernelGGL(indexer_fp32_kernel, dim3((unsigned)blocks), dim3(256),
+                       shm, s, static_cast<const float*>(q), weights,
+                       static_cast<const uint8_t*>(k_index_cache), num_pages,
+                       real_page_table, rpt_stride, token_to_req,
+                       seqlens_expanded, max_seqlen_k, logits, logits_stride,
+                       Hi, Di, chunks);
+  }
+  return nsa::check_launch(fn);
+}

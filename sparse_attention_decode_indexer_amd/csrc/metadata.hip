@@ -1,0 +1,187 @@
+// a0: per-forward metadata of the sparse attention step in one launch.
+//
+// Follows the metadata construction of "nsa_backend.py (EngineX-Hygon sglang
+// fork)" (NSAMetadata, compute_cu_seqlens, _transform_table_1_to_real,
+// NativeSparseAttnBackend.init_forward_metadata) and "dsa_backend.py (sglang
+// main)" (DeepseekSparseAttnBackend.init_forward_metadata: decode,
+// target-verify and extend branches). The pages build these tensors with a
+// chain of torch ops plus a host sync for max(seq_lens); here one kernel
+// writes all of them with the bound given by the host.
+//
+// Launch shape: one 256-thread block per request. A block needs three
+// exclusive prefix sums over the requests before it (KV lengths, query
+// rows, clipped lengths); it recomputes them itself (O(bs) per block), which
+// avoids a second launch or a grid-wide barrier. The clipped-length sum of
+// one request has a closed form: its query rows see a, a+1, ..., a+n-1 KV
+// tokens, so sum_j min(a+j, K) = m*a + m(m-1)/2 + (n-m)*K with
+// m = clamp(K-a, 0, n).
+#include "common.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxBatch = 16384;
+
+__device__ __forceinline__ long long clipped_sum(long long a, long long n,
+                                                 long long k) {
+  long long m = k - a;
+  m = m < 0 ? 0 : (m > n ? n : m);
+  return m * a + m * (m - 1) / 2 + (n - m) * k;
+}
+
+__device__ __forceinline__ int q_rows_of(int mode, int draft,
+                                         const int32_t* extend_lens, int i) {
+  if (mode == NSA_MODE_DECODE) return 1;
+  if (mode == NSA_MODE_TARGET_VERIFY) return draft;
+  return extend_lens[i];
+}
+
+__device__ long long block_sum(long long v, long long* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  long long r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kThreads)
+build_metadata_kernel(int mode, int bs, int draft, int topk,
+                      const int32_t* __restrict__ seq_lens,
+                      const int32_t* __restrict__ extend_lens,
+                      const int32_t* __restrict__ req_to_token,
+                      int64_t rtt_stride,
+                      const int32_t* __restrict__ req_pool_indices,
+                      int max_seqlen_k, int T, int32_t* cache_seqlens,
+                      int32_t* cu_seqlens_k, int32_t* cu_seqlens_q,
+                      int32_t* seqlens_expanded, int32_t* nsa_cache_seqlens,
+                      int32_t* nsa_cu_seqlens_k, int32_t* nsa_cu_seqlens_q,
+                      int32_t* real_page_table, int64_t rpt_stride,
+                      int32_t* token_to_req, int32_t* page_table_1,
+                      int64_t pt1_stride) {
+  __shared__ long long red[kThreads];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int d = (mode == NSA_MODE_TARGET_VERIFY) ? draft : 0;
+
+  // exclusive prefix sums over requests 0..r-1
+  long long pk = 0, pq = 0, pn = 0;
+  const int upto = r < bs ? r : bs;
+  for (int i = tid; i < upto; i += kThreads) {
+    const long long kv = (long long)seq_lens[i] + d;
+    const long long ql = q_rows_of(mode, draft, extend_lens, i);
+    pk += kv;
+    pq += ql;
+    pn += clipped_sum(kv - ql + 1, ql, topk);
+  }
+  pk = block_sum(pk, red);
+  pq = block_sum(pq, red);
+  pn = block_sum(pn, red);
+
+  if (r == 0 && tid == 0) {
+    cu_seqlens_k[0] = 0;
+    cu_seqlens_q[0] = 0;
+    nsa_cu_seqlens_k[0] = 0;
+    nsa_cu_seqlens_q[0] = 0;
+  }
+  if (r >= bs) return;
+
+  const int kv = seq_lens[r] + d;
+  const int ql = q_rows_of(mode, draft, extend_lens, r);
+  const long long a = (long long)kv - ql + 1;  // visible length of row 0
+  if (tid == 0) {
+    cache_seqlens[r] = kv;
+    cu_seqlens_k[r + 1] = (int32_t)(pk + kv);
+    if (mode == NSA_MODE_EXTEND) cu_seqlens_q[r + 1] = (int32_t)(pq + ql);
+  }
+  for (int j = tid; j < ql; j += kThreads) {
+    const long long t = pq + j;
+    if (t >= T) break;
+    const long long se = a + j;
+    seqlens_expanded[t] = (int32_t)se;
+    nsa_cache_seqlens[t] = (int32_t)(se < topk ? se : topk);
+    nsa_cu_seqlens_k[t + 1] = (int32_t)(pn + clipped_sum(a, j + 1, topk));
+    nsa_cu_seqlens_q[t + 1] = (int32_t)(t + 1);
+    token_to_req[t] = r;
+    if (mode != NSA_MODE_EXTEND) cu_seqlens_q[t + 1] = (int32_t)(t + 1);
+  }
+
+  // page-granular table: every 64th entry of the request's token table,
+  // divided by 64 (arithmetic shift = floor division)
+  const int32_t* row = req_to_token + (int64_t)req_pool_indices[r] * rtt_stride;
+  const int ncols = (max_seqlen_k + NSA_PAGE_SIZE - 1) / NSA_PAGE_SIZE;
+  int32_t* rpt = real_page_table + (int64_t)r * rpt_stride;
+  for (int p = tid; p < ncols; p += kThreads)
+    rpt[p] = row[(int64_t)p * NSA_PAGE_SIZE] >> 6;
+  if (page_table_1 != nullptr) {
+    int32_t* pt = page_table_1 + (int64_t)r * pt1_stride;
+    for (int c = tid; c < max_seqlen_k; c += kThreads) pt[c] = row[c];
+  }
+}
+
+}  // namespace
+
+extern "C" int nsa_build_metadata(
+    int mode, int bs, int draft_token_num, int topk, int page_size,
+    const int32_t* seq_lens, const int32_t* extend_lens,
+    const int32_t* req_to_token, int64_t rtt_stride,
+    const int32_t* req_pool_indices, int max_seqlen_k, int num_q_rows,
+    int32_t* cache_seqlens, int32_t* cu_seqlens_k, int32_t* cu_seqlens_q,
+    int32_t* seqlens_expanded, int32_t* nsa_cache_seqlens,
+    int32_t* nsa_cu_seqlens_k, int32_t* nsa_cu_seqlens_q,
+    int32_t* real_page_table, int64_t rpt_stride, int32_t* token_to_req,
+    int32_t* page_table_1, int64_t pt1_stride, void* stream) {
+  const char* fn = "nsa_build_metadata";
+  NSA_REQUIRE(mode == NSA_MODE_DECODE || mode == NSA_MODE_EXTEND ||
+                  mode == NSA_MODE_TARGET_VERIFY,
+              NSA_ERR_INVALID_ARG, "%s: unknown mode %d", fn, mode);
+  NSA_REQUIRE(bs >= 0 && bs <= kMaxBatch, NSA_ERR_UNSUPPORTED,
+              "%s: bs %d outside [0, %d]", fn, bs, kMaxBatch);
+  NSA_REQUIRE(topk > 0, NSA_ERR_INVALID_ARG, "%s: topk %d <= 0", fn, topk);
+  NSA_REQUIRE(page_size == NSA_PAGE_SIZE, NSA_ERR_UNSUPPORTED,
+              "%s: page_size %d (only 64 is supported)", fn, page_size);
+  NSA_REQUIRE(max_seqlen_k >= 0 && num_q_rows >= 0, NSA_ERR_INVALID_ARG,
+              "%s: negative max_seqlen_k or num_q_rows", fn);
+  if (mode == NSA_MODE_TARGET_VERIFY) {
+    NSA_REQUIRE(draft_token_num >= 1, NSA_ERR_INVALID_ARG,
+                "%s: target-verify needs draft_token_num >= 1", fn);
+    NSA_REQUIRE((int64_t)num_q_rows == (int64_t)bs * draft_token_num,
+                NSA_ERR_INVALID_ARG,
+                "%s: num_q_rows %d != bs * draft_token_num", fn, num_q_rows);
+  } else if (mode == NSA_MODE_DECODE) {
+    NSA_REQUIRE(num_q_rows == bs, NSA_ERR_INVALID_ARG,
+                "%s: decode needs num_q_rows == bs", fn);
+  } else {
+    NSA_REQUIRE(extend_lens != nullptr, NSA_ERR_INVALID_ARG,
+                "%s: extend needs extend_lens", fn);
+  }
+  NSA_REQUIRE(cache_seqlens && cu_seqlens_k && cu_seqlens_q &&
+                  seqlens_expanded && nsa_cache_seqlens && nsa_cu_seqlens_k &&
+                  nsa_cu_seqlens_q && real_page_table && token_to_req,
+              NSA_ERR_INVALID_ARG, "%s: null output pointer", fn);
+  NSA_REQUIRE(bs == 0 || (seq_lens && req_to_token && req_pool_indices),
+              NSA_ERR_INVALID_ARG, "%s: null input pointer", fn);
+  const int64_t ncols = (max_seqlen_k + NSA_PAGE_SIZE - 1) / NSA_PAGE_SIZE;
+  NSA_REQUIRE(rtt_stride >= max_seqlen_k, NSA_ERR_INVALID_ARG,
+              "%s: rtt_stride %lld < max_seqlen_k %d", fn,
+              (long long)rtt_stride, max_seqlen_k);
+  NSA_REQUIRE(rpt_stride >= ncols, NSA_ERR_INVALID_ARG,
+              "%s: rpt_stride %lld < ceil(max_seqlen_k/64) = %lld", fn,
+              (long long)rpt_stride, (long long)ncols);
+  NSA_REQUIRE(page_table_1 == nullptr || pt1_stride >= max_seqlen_k,
+              NSA_ERR_INVALID_ARG, "%s: pt1_stride < max_seqlen_k", fn);
+
+  const int grid = bs > 0 ? bs : 1;
+  hipLaunchKernelGGL(build_metadata_kernel, dim3(grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, mode, bs, draft_token_num, topk,
+                     seq_lens, extend_lens, req_to_token, rtt_stride,
+                     req_pool_indices, max_seqlen_k, num_q_rows, cache_seqlens,
+                     cu_seqlens_k, cu_seqlens_q, seqlens_expanded,
+                     nsa_cache_seqlens, nsa_cu_seqlens_k, nsa_cu_seqlens_q,
+                     real_page_table, rpt_stride, token_to_req, page_table_1,
+                     pt1_stride);
+  return nsa::check_launch(fn);
+}

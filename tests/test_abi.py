@@ -1,0 +1,141 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/nsa.h declares, and rejects bad arguments with status
+codes before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_decode_indexer_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+N = None  # NULL
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "nsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_decode_indexer_amd.build import build_library
+        build_library()
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of date"
+
+
+def test_version_and_empty_error(lib):
+    assert lib.nsa_version() >= 100
+    assert isinstance(lib.nsa_last_error(), bytes)
+
+
+def _err(lib):
+    return lib.nsa_last_error().decode()
+
+
+def test_metadata_rejects_bad_arguments(lib):
+    out = [ctypes.c_void_p(16)] * 8
+    # unknown mode
+    assert lib.nsa_build_metadata(7, 1, 0, 8, 64, 16, N, 16, 64, 16, 64, 1,
+                                  *out, 1, 16, N, 0, N) == -1
+    assert "mode" in _err(lib)
+    # page size
+    assert lib.nsa_build_metadata(0, 1, 0, 8, 32, 16, N, 16, 64, 16, 64, 1,
+                                  *out, 1, 16, N, 0, N) == -2
+    # decode needs num_q_rows == bs
+    assert lib.nsa_build_metadata(0, 2, 0, 8, 64, 16, N, 16, 64, 16, 64, 3,
+                                  *out, 1, 16, N, 0, N) == -1
+    # verify needs bs * draft rows
+    assert lib.nsa_build_metadata(2, 2, 3, 8, 64, 16, N, 16, 64, 16, 64, 5,
+                                  *out, 1, 16, N, 0, N) == -1
+    # extend needs extend_lens
+    assert lib.nsa_build_metadata(1, 2, 0, 8, 64, 16, N, 16, 64, 16, 64, 5,
+                                  *out, 1, 16, N, 0, N) == -1
+    # real_page_table stride too small for max_seqlen_k = 200 (needs 4)
+    assert lib.nsa_build_metadata(0, 1, 0, 8, 64, 16, N, 16, 256, 16, 200, 1,
+                                  *out, 3, 16, N, 0, N) == -1
+    assert "rpt_stride" in _err(lib)
+
+
+def test_indexer_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(256)
+    # fp8 path supports only 64 heads x 128 dims
+    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 10, p, 4, p, p, 4, 32, 128, 64,
+                                  200, p, 256, N) == -2
+    # mismatched dtypes
+    assert lib.nsa_indexer_logits(p, 2, p, p, 0, 10, p, 4, p, p, 4, 64, 128, 64,
+                                  200, p, 256, N) == -2
+    # logits stride below max_seqlen_k
+    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 10, p, 4, p, p, 4, 64, 128, 64,
+                                  200, p, 100, N) == -1
+    # misaligned q
+    assert lib.nsa_indexer_logits(ctypes.c_void_p(257), 2, p, p, 2, 10, p, 4, p,
+                                  p, 4, 64, 128, 64, 200, p, 256, N) == -1
+
+
+def test_topk_and_transform_reject_bad_arguments(lib):
+    p = ctypes.c_void_p(256)
+    assert lib.nsa_topk_transform(p, 100, p, 4, 0, 100, N, 0, N, 64, p, 16, N, 0,
+                                  N) == -1                      # topk 0
+    assert lib.nsa_topk_transform(p, 100, p, 4, 16, 100, p, 1, p, 64, p, 16, N, 0,
+                                  N) == -1                      # table stride
+    assert lib.nsa_topk_transform(p, 100, p, 4, 16, 100, N, 0, N, 64, p, 8, N, 0,
+                                  N) == -1                      # out stride
+    # exactly one table
+    assert lib.nsa_page_table_transform(p, 8, 2, 8, p, 8, 8, p, 8, 8, 64, p, p, 8,
+                                        N) == -1
+    assert lib.nsa_page_table_transform(p, 8, 2, 8, N, 0, 0, N, 0, 0, 64, p, p, 8,
+                                        N) == -1
+    # zero rows is a no-op
+    assert lib.nsa_topk_transform(N, 0, N, 0, 8, 0, N, 0, N, 64, N, 8, N, 0, N) == 0
+    ws = ctypes.c_size_t(99)
+    assert lib.nsa_topk_workspace_size(4, 100, 16, ctypes.byref(ws)) == 0
+
+
+def test_sparse_mla_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(256)
+    args = lambda **kw: dict(dict(q=p, ts=128 * 576, hs=576, kv=p, kvd=0, ns=1000,  # noqa: E731
+                                  idx=p, istr=2048, sl=N, T=2, H=128, topk=2048,
+                                  dqk=576, dv=512, sc=0.1, out=p, lse=N, ws=p,
+                                  wsb=1 << 30, st=N), **kw)
+    call = lambda a: lib.nsa_sparse_mla_decode(*a.values())  # noqa: E731
+    assert call(args(H=24)) == -2              # not a multiple of 16
+    assert call(args(H=144, ts=144 * 576)) == -2
+    assert call(args(dqk=512)) == -2
+    assert call(args(kvd=5)) == -2
+    assert call(args(istr=1024)) == -1         # index stride < topk
+    assert call(args(q=ctypes.c_void_p(258))) == -1
+    assert call(args(hs=570)) == -1
+    assert call(args(ws=N, wsb=0)) == -3       # decode plan needs a workspace
+    assert "workspace" in _err(lib)
+    size = ctypes.c_size_t(0)
+    assert lib.nsa_sparse_mla_workspace_size(2, 128, 2048, 512, ctypes.byref(size)) == 0
+    assert size.value > 0
+    assert lib.nsa_sparse_mla_workspace_size(2, 100, 2048, 512, ctypes.byref(size)) == -1
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(256)
+    assert lib.nsa_quantize_k_cache(p, 10, 500, p, N) == -1      # stride < 576
+    assert lib.nsa_quantize_k_cache(ctypes.c_void_p(8), 10, 576, p, N) == -1
+    assert lib.nsa_quantize_k_cache(N, 0, 576, N, N) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import sparse_attention_decode_indexer_amd as nsa
+    with pytest.raises(ValueError):
+        nsa.nsa_quantize_k_cache(torch.zeros(4, 576, dtype=torch.bfloat16))

@@ -1,0 +1,119 @@
+"""GPU parity: nsa_quantize_k_cache (bit-exact) and nsa_indexer_logits
+(within the fp32-summation tolerance) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import oracle
+from helpers import (DEV, need_gpu, note, to_dev, oracle_metadata, gpu_metadata,
+                     idx_dtype, oracle_logits_rows, check_logits, full_workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _special_rows(n, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(n, 576, generator=g)
+    x[0] = 0.0                                   # all-zero row
+    x[1, :128] = -0.0                            # negative zeros block
+    x[2] *= 1e-30                                # tiny values (subnormal codes)
+    x[3, 5] = 1e4                                # one dominant value per block
+    x[4] = torch.linspace(-3, 3, 576)
+    x[5, 130] = 7.0
+    x[6:] *= torch.exp(torch.randn(n - 6, 1, generator=g) * 4)   # magnitude spread
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("n", [1, 7, 4096])
+def test_quantize_bit_exact(n):
+    nsa = need_gpu()
+    note(f"quantize n={n}")
+    x = _special_rows(max(n, 7))[:n]
+    got = nsa.nsa_quantize_k_cache(x.to(DEV)).cpu().numpy()
+    want = oracle.quant.quantize_k_cache(x.view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_quantize_strided_rows():
+    nsa = need_gpu()
+    x = _special_rows(64, seed=3)
+    big = torch.zeros(64, 640, dtype=torch.bfloat16)
+    big[:, :576] = x
+    got = nsa.nsa_quantize_k_cache(big.to(DEV)[:, :576]).cpu().numpy()
+    want = oracle.quant.quantize_k_cache(x.view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_quantize_full_cache_sampled():
+    nsa = need_gpu()
+    w = full_workload("decode_b128")
+    note(f"quantize full decode_b128 cache: {w.kv_bf16.shape[0]} slots")
+    q8 = nsa.nsa_quantize_k_cache(w.kv_bf16)
+    rng = np.random.default_rng(0)
+    rows = np.concatenate([[0, w.kv_bf16.shape[0] - 1],
+                           rng.integers(0, w.kv_bf16.shape[0], 2000)])
+    ri = torch.as_tensor(rows, device=DEV)
+    want = oracle.quant.quantize_k_cache(
+        w.kv_bf16[ri].view(torch.int16).cpu().numpy().view(np.uint16))
+    np.testing.assert_array_equal(q8[ri].cpu().numpy(), want)
+
+
+def _indexer_case(nsa, w, rows=None):
+    md = gpu_metadata(nsa, w)
+    ref = oracle_metadata(w)
+    logits = nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
+                                    md["real_page_table"], md["token_to_req"],
+                                    md["seqlens_expanded"], w.max_seqlen_k,
+                                    dtype=idx_dtype(nsa, w))
+    torch.cuda.synchronize()
+    rows = list(range(w.num_rows)) if rows is None else rows
+    want = oracle_logits_rows(w, ref, rows)
+    for t in rows:
+        L = int(ref["seqlens_expanded"][t])
+        check_logits(logits[t].cpu().numpy(), want[t], L, what=f"{w.name} row {t}")
+    return logits
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="tiny"),
+    dict(name="decode_b32", bs=4, seqlen_range=(1, 3000)),
+    dict(name="decode_b32", bs=3, seqlen_range=(2047, 2049)),
+    dict(name="verify", bs=3, seqlen_range=(100, 4000)),
+    dict(name="extend", bs=2, extend_lens=[3, 40], prefix_lens=[5, 2100]),
+    dict(name="tiny", seq_lens=[1, 65], idx_heads=3, idx_dim=12),
+])
+def test_indexer_small(case):
+    nsa = need_gpu()
+    case = dict(case)
+    name = case.pop("name")
+    note(f"indexer {name} {case}")
+    w = to_dev(W.make_workload(name, parts=("indexer",), **case))
+    _indexer_case(nsa, w)
+
+
+def test_indexer_invalid_pages_give_neg_inf():
+    nsa = need_gpu()
+    w = to_dev(W.make_workload("decode_b32", parts=("indexer",), bs=2,
+                               seqlen_range=(300, 300)))
+    md = gpu_metadata(nsa, w)
+    rpt = md["real_page_table"].clone()
+    rpt[0, 1] = -5
+    rpt[1, 2] = w.num_pages + 10
+    logits = nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache, rpt,
+                                    md["token_to_req"], md["seqlens_expanded"],
+                                    w.max_seqlen_k).cpu().numpy()
+    assert np.isneginf(logits[0, 64:128]).all() and np.isfinite(logits[0, :64]).all()
+    assert np.isneginf(logits[1, 128:192]).all() and np.isfinite(logits[1, 192:300]).all()
+
+
+@pytest.mark.parametrize("name", ["decode_b128", "verify"])
+def test_indexer_full_size_sampled_rows(name):
+    nsa = need_gpu()
+    w = full_workload(name)
+    note(f"indexer full {name}: T={w.num_rows} max_L={w.max_seqlen_k}")
+    ref = oracle_metadata(w)
+    L = ref["seqlens_expanded"]
+    rows = sorted({int(np.argmax(L)), int(np.argmin(L)), w.num_rows - 1})
+    _indexer_case(nsa, w, rows=rows)

@@ -1,0 +1,177 @@
+"""GPU parity: nsa_topk_transform (exact selection on oracle-made logits;
+acceptance on the GPU's own logits) and nsa_sparse_mla_decode / _extend
+(against the oracle given identical indices)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (DEV, need_gpu, note, check_topk_row, check_attention,
+                     CacheFromRows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _topk_rows(rng, lengths, width, kind):
+    x = np.full((len(lengths), width), np.nan, np.float32)   # unwritten tail
+    for t, L in enumerate(lengths):
+        if kind == "normal":
+            x[t, :L] = rng.normal(size=L) * 20 + 40
+        elif kind == "ties":
+            x[t, :L] = rng.integers(0, 7, size=L).astype(np.float32)
+        elif kind == "const":
+            x[t, :L] = 3.0
+        elif kind == "special":
+            v = rng.normal(size=L).astype(np.float32)
+            v[rng.random(L) < 0.05] = -np.inf
+            v[rng.random(L) < 0.05] = np.nan
+            v[rng.random(L) < 0.01] = np.inf
+            v[rng.random(L) < 0.1] = -0.0
+            x[t, :L] = v
+    return x
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "const", "special"])
+@pytest.mark.parametrize("topk", [256, 2048])
+def test_topk_exact_on_given_logits(kind, topk):
+    nsa = need_gpu()
+    note(f"topk exact {kind} topk={topk}")
+    rng = np.random.default_rng(topk)
+    lengths = [0, 1, topk - 1, topk, topk + 1, 3 * topk + 5, 20000, 131072 - 3]
+    width = max(lengths) + 7
+    x = _topk_rows(rng, lengths, width, kind)
+    lg = torch.as_tensor(x, device=DEV)
+    ln = torch.as_tensor(lengths, dtype=torch.int32, device=DEV)
+    got = nsa.nsa_topk_transform(lg, ln, topk, width).cpu().numpy()
+    for t, L in enumerate(lengths):
+        sel = got[t]
+        check_topk_row(sel, L, topk, what=f"row {t}")
+        # both sides break ties by position and rank NaN lowest: equal sets
+        want = oracle.topk.topk_row(x[t].astype(np.float64), L, topk)
+        want = np.sort(want[want >= 0])
+        np.testing.assert_array_equal(sel[:len(want)], want, err_msg=f"row {t} L={L}")
+
+
+def test_topk_fused_table_and_strides():
+    nsa = need_gpu()
+    rng = np.random.default_rng(1)
+    lengths = [5000, 100, 7000]
+    width = 7040
+    x = _topk_rows(rng, lengths, width, "normal")
+    big = torch.zeros(3, width + 64, device=DEV)
+    big[:, :width] = torch.as_tensor(x, device=DEV)
+    lg = big[:, :width]                                    # row stride > width
+    ln = torch.as_tensor(lengths, dtype=torch.int32, device=DEV)
+    table = torch.as_tensor(rng.permutation(500)[:2 * 110].reshape(2, 110),
+                            dtype=torch.int32, device=DEV)
+    t2r = torch.tensor([1, 0, 1], dtype=torch.int32, device=DEV)
+    logical = nsa.nsa_topk_transform(lg, ln, 2048, width).cpu().numpy()
+    slots = nsa.nsa_topk_transform(lg, ln, 2048, width, table=table,
+                                   token_to_req=t2r).cpu().numpy()
+    want = oracle.transform.transform_compact(logical, table.cpu().numpy(), [1, 0, 1])
+    np.testing.assert_array_equal(slots, want)
+
+
+def _random_case(rng, T, H, topk, num_slots, kind, frac_pad=0.1):
+    q = torch.randn(T, H, 576, generator=torch.Generator().manual_seed(int(rng.integers(1 << 30))))
+    q = q.to(torch.bfloat16)
+    kv = torch.randn(num_slots, 576, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    bits = kv.view(torch.int16).numpy().view(np.uint16)
+    if kind == "fp8":
+        raw = oracle.quant.quantize_k_cache(bits)
+        cache_dev = torch.as_tensor(raw, device=DEV)
+        vals = oracle.quant.dequantize_rows(raw)
+    else:
+        cache_dev = kv.to(DEV)
+        vals = oracle.formats.bf16_bits_to_f64(bits)
+    idx = np.full((T, topk), -1, np.int64)
+    for t in range(T):
+        n = int(topk * (1 - frac_pad * rng.random()))
+        idx[t, :n] = rng.choice(num_slots, size=n, replace=False)
+        if t % 3 == 1:
+            rng.shuffle(idx[t])       # -1 interleaved
+    return q, cache_dev, vals, idx
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("T,H,topk", [(1, 16, 2048), (3, 128, 2048), (5, 64, 256),
+                                      (2, 32, 100), (40, 16, 64), (4, 48, 512)])
+def test_sparse_mla_decode(kind, T, H, topk):
+    nsa = need_gpu()
+    note(f"sparse_mla {kind} T={T} H={H} topk={topk}")
+    rng = np.random.default_rng(T * 1000 + H + topk)
+    q, cache, vals, idx = _random_case(rng, T, H, topk, 6000, kind)
+    kvd = nsa.KV_FP8_656 if kind == "fp8" else nsa.KV_BF16_576
+    out, lse = nsa.nsa_sparse_mla_decode(q.to(DEV), cache, kvd,
+                                         torch.as_tensor(idx, dtype=torch.int32, device=DEV),
+                                         0.0721)
+    o_ref, lse_ref = oracle.sparse_mla.sparse_mla(q.to(torch.float64).numpy(),
+                                                  CacheFromRows(dict(enumerate(vals))),
+                                                  idx, 0.0721)
+    check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, kind)
+
+
+def test_sparse_mla_seqlens_invalid_slots_and_empty_rows():
+    nsa = need_gpu()
+    rng = np.random.default_rng(3)
+    T, H, topk, S = 6, 16, 512, 3000
+    q, cache, vals, idx = _random_case(rng, T, H, topk, S, "bf16", frac_pad=0.0)
+    idx[1, :] = -1                      # empty row
+    idx[2, 7] = S + 5                   # out of range: ignored
+    idx[2, 9] = -7
+    idx[3, 1:] = -1                     # one slot
+    seqlens = np.array([topk, topk, topk, topk, 33, 0], np.int32)
+    out, lse = nsa.nsa_sparse_mla_decode(
+        q.to(DEV), cache, nsa.KV_BF16_576,
+        torch.as_tensor(idx, dtype=torch.int32, device=DEV), 0.1,
+        nsa_cache_seqlens=torch.as_tensor(seqlens, device=DEV))
+    clean = np.where((idx >= 0) & (idx < S), idx, -1)
+    o_ref, lse_ref = oracle.sparse_mla.sparse_mla(q.to(torch.float64).numpy(),
+                                                  CacheFromRows(dict(enumerate(vals))),
+                                                  clean, 0.1, nsa_cache_seqlens=seqlens)
+    o = out.float().cpu().numpy()
+    check_attention(o, lse.cpu().numpy(), o_ref, lse_ref, "bf16")
+    assert (o[1] == 0).all() and (o[5] == 0).all()
+    assert np.isneginf(lse.cpu().numpy()[[1, 5]]).all()
+    np.testing.assert_allclose(o[3], np.broadcast_to(vals[idx[3, 0], :512], (H, 512)),
+                               rtol=1e-2, atol=1e-2)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_sparse_mla_extend_entry(kind):
+    nsa = need_gpu()
+    note(f"sparse_mla extend {kind}")
+    rng = np.random.default_rng(11)
+    T, H, topk = 300, 16, 256
+    q, cache, vals, idx = _random_case(rng, T, H, topk, 4000, kind)
+    kvd = nsa.KV_FP8_656 if kind == "fp8" else nsa.KV_BF16_576
+    idx_d = torch.as_tensor(idx, dtype=torch.int32, device=DEV)
+    out, lse = nsa.nsa_sparse_mla_extend(q.to(DEV), cache, kvd, idx_d, 0.05)
+    rows = [0, 1, 150, 299]
+    o_ref, lse_ref = oracle.sparse_mla.sparse_mla(q[rows].to(torch.float64).numpy(),
+                                                  CacheFromRows(dict(enumerate(vals))),
+                                                  idx[rows], 0.05)
+    check_attention(out.float().cpu().numpy()[rows], lse.cpu().numpy()[rows],
+                    o_ref, lse_ref, kind)
+    # the decode entry computes the same function
+    out2, _ = nsa.nsa_sparse_mla_decode(q.to(DEV), cache, kvd, idx_d, 0.05)
+    check_attention(out2.float().cpu().numpy()[rows], None, o_ref, lse_ref, kind)
+
+
+def test_sparse_mla_strided_q_and_determinism():
+    nsa = need_gpu()
+    rng = np.random.default_rng(5)
+    T, H, topk = 4, 128, 2048
+    q, cache, vals, idx = _random_case(rng, T, H, topk, 5000, "bf16")
+    qbig = torch.zeros(T, H, 640, dtype=torch.bfloat16)
+    qbig[:, :, :576] = q
+    qd = qbig.to(DEV)[:, :, :576]
+    idx_d = torch.as_tensor(idx, dtype=torch.int32, device=DEV)
+    a, la = nsa.nsa_sparse_mla_decode(qd, cache, nsa.KV_BF16_576, idx_d, 0.07)
+    b, lb = nsa.nsa_sparse_mla_decode(q.to(DEV), cache, nsa.KV_BF16_576, idx_d, 0.07)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    o_ref, lse_ref = oracle.sparse_mla.sparse_mla(q.to(torch.float64).numpy(),
+                                                  CacheFromRows(dict(enumerate(vals))),
+                                                  idx, 0.07)
+    check_attention(a.float().cpu().numpy(), la.cpu().numpy(), o_ref, lse_ref, "bf16")

@@ -103,11 +103,15 @@ def _fp8_codes(x):
     return x.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def make_workload(name, device="cpu", seed=0, **overrides):
+def make_workload(name, device="cpu", seed=0, parts=("indexer", "attention"),
+                  **overrides):
     """Build one workload on ``device`` with a seeded torch generator.
 
     ``overrides`` replace entries of the configuration (e.g. ``bs`` or
-    ``seqlen_range``) for reduced-size parity cases.
+    ``seqlen_range``) for reduced-size parity cases. ``parts`` selects the
+    large inputs to draw: "indexer" (q, weights, index-key cache) and
+    "attention" (MLA q and the bf16 latent cache); metadata inputs are always
+    drawn first, so they do not depend on ``parts``.
     """
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)
@@ -162,6 +166,26 @@ def make_workload(name, device="cpu", seed=0, **overrides):
     w.req_pool_indices = row_of_req.to(torch.int32).to(dev)
 
     T, Hi, Di = num_rows, w.idx_heads, w.idx_dim
+    if "indexer" in parts:
+        _draw_indexer(w, gen, dev, T, Hi, Di, num_pages)
+    if "attention" in parts:
+        gen_a = torch.Generator(device=dev)
+        gen_a.manual_seed(seed + 1000003)
+        w.q = torch.randn(T, w.heads, D_QK, generator=gen_a, device=dev).to(torch.bfloat16)
+        w.kv_bf16 = _randn_bf16(num_pages * PAGE, D_QK, gen_a, dev)
+    return w
+
+
+def _randn_bf16(rows, cols, gen, dev, chunk=1 << 20):
+    """N(0,1) rounded to bf16, drawn in row chunks (bounded fp32 temporaries)."""
+    out = torch.empty(rows, cols, dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, rows, chunk):
+        r1 = min(rows, r0 + chunk)
+        out[r0:r1] = torch.randn(r1 - r0, cols, generator=gen, device=dev)
+    return out
+
+
+def _draw_indexer(w, gen, dev, T, Hi, Di, num_pages):
     if w.idx_kind == "fp8":
         w.q_idx = _fp8_codes(torch.randn(T, Hi, Di, generator=gen, device=dev) * 0.5)
         keys = _fp8_codes(torch.randn(num_pages, PAGE * Di, generator=gen,
@@ -177,12 +201,6 @@ def make_workload(name, device="cpu", seed=0, **overrides):
         [keys.reshape(num_pages, -1),
          kscale.to(torch.float32).contiguous().view(torch.uint8).reshape(num_pages, -1)],
         dim=1).contiguous()
-
-    H = w.heads
-    w.q = torch.randn(T, H, D_QK, generator=gen, device=dev).to(torch.bfloat16)
-    w.kv_bf16 = torch.randn(num_pages * PAGE, D_QK, generator=gen,
-                            device=dev).to(torch.bfloat16)
-    return w
 
 
 def host_inputs(w):
