@@ -1,0 +1,281 @@
+"""Benchmark of the sparse-attention decode step on one MI355X.
+
+A step is one pass of the whole path over one batch: metadata, indexer
+logits, fused top-k + page transform, sparse MLA. The default workload is the
+decode batch of 128 requests with KV lengths uniform in [32768, 131072],
+topk 2048, 128 MLA heads over an fp8 block-scaled latent cache and a 64-head
+x 128-dim fp8 indexer. Inputs are synthetic, seeded and resident in HBM
+before timing starts.
+
+Prints one JSON line. `value` is query rows (tokens) per second over the
+timed steps; `roofline` is for the dominant kernel (the indexer), with its
+algorithmic bytes per launch divided by its average launch time, measured
+with HIP events on the launch stream; `cpu_baseline` is the CPU oracle timed
+on a bounded sample of rows of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "query-tokens/s through indexer+topk+sparse MLA; % of HBM roofline"
+PMC_FILE = os.path.join(ROOT, "profiles", "indexer_fp8_decode_b128_pmc.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_b128",
+                    choices=["decode_b128", "decode_b32", "verify", "extend"])
+    ap.add_argument("--cpu-rows", type=int, default=8,
+                    help="rows of the oracle sample (0 = skip the CPU leg)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (a known-size "
+                         "kernel for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def indexer_bytes(lengths, hi=64, di=128):
+    """Algorithmic bytes of one indexer launch: per row the q row and weights,
+    one page-table entry per 64 positions, and per position the fp8 key,
+    its fp32 scale and the fp32 logit written."""
+    b = 0
+    for L in lengths:
+        L = int(L)
+        b += hi * di + hi * 4 + ((L + 63) // 64) * 4 + L * (di + 4 + 4)
+    return b
+
+
+def pipeline_bytes(lengths, topk, heads, kv_row_bytes, hi=64, di=128):
+    """Strict algorithmic bytes of one step: index keys + scales, q / w, the
+    page-table row, the selected latent rows, MLA q and output."""
+    b = 0
+    for L in lengths:
+        L = int(L)
+        n = min(L, topk)
+        b += hi * di + hi * 4 + ((L + 63) // 64) * 4 + L * (di + 4)
+        b += n * kv_row_bytes + heads * 576 * 2 + heads * 512 * 2 + heads * 4
+    return b
+
+
+def read_pmc(expected_sha):
+    """HBM traffic of the indexer from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    kv = {}
+    for line in open(PMC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("indexer_source_sha256") != expected_sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, rows):
+    """The oracle, as it stands, on `rows` query rows of the same workload:
+    metadata for the batch, then per row indexer -> top-k -> transform ->
+    sparse MLA. Returns rows/s, threads used and the sample description."""
+    import numpy as np
+    import torch
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    h = {k: getattr(w, k).cpu().numpy() if getattr(w, k) is not None else None
+         for k in ("seq_lens", "extend_lens", "req_to_token", "req_pool_indices")}
+    sample = list(range(0, w.num_rows, max(1, w.num_rows // rows)))[:rows]
+    # inputs of the sampled rows, copied to the host before the clock starts
+    md0 = oracle.metadata.build_metadata(w.mode, h["seq_lens"], h["req_to_token"],
+                                         h["req_pool_indices"], w.topk,
+                                         extend_lens=h["extend_lens"],
+                                         draft_token_num=w.draft)
+    per_row = []
+    for t in sample:
+        r = int(md0["token_to_req"][t])
+        L = int(md0["seqlens_expanded"][t])
+        pages = md0["real_page_table"][r, :(L + 63) // 64]
+        raw_idx = w.index_cache[torch.as_tensor(pages, device=w.index_cache.device)].cpu().numpy()
+        slots_all = md0["page_table_1"][r, :L]
+        per_row.append(dict(t=t, r=r, L=L, raw_idx=raw_idx,
+                            q_idx=w.q_idx[t:t + 1].cpu().numpy(),
+                            wts=w.idx_weights[t:t + 1].cpu().numpy(),
+                            q=w.q[t:t + 1].to(torch.float64).cpu().numpy(),
+                            slots_all=slots_all))
+    kv_rows = {}
+    for pr in per_row:
+        s = torch.as_tensor(pr["slots_all"], device=w.kv_bf16.device)
+        kv_rows[pr["t"]] = w.kv_bf16[s].view(torch.int16).cpu().numpy().view(np.uint16)
+
+    t0 = time.perf_counter()
+    md = oracle.metadata.build_metadata(w.mode, h["seq_lens"], h["req_to_token"],
+                                        h["req_pool_indices"], w.topk,
+                                        extend_lens=h["extend_lens"],
+                                        draft_token_num=w.draft)
+    for pr in per_row:
+        keys, ks = oracle.indexer.decode_index_pages(pr["raw_idx"], w.idx_dim, w.idx_kind)
+        q64 = (oracle.formats.e4m3_decode(pr["q_idx"]) if w.idx_kind == "fp8"
+               else pr["q_idx"].astype(np.float64))
+        npg = (pr["L"] + 63) // 64
+        logits = oracle.indexer.indexer_logits(q64, pr["wts"], keys, ks,
+                                               np.arange(npg)[None], [0], [pr["L"]],
+                                               pr["L"])
+        sel = oracle.topk.topk(logits, [pr["L"]], w.topk)
+        slots = oracle.transform.transform_compact(sel, md["real_page_table"],
+                                                   [pr["r"]])
+        # the latent cache rows the row reads, in the cache's stored format
+        pos = sel[0][sel[0] >= 0]
+        bits = kv_rows[pr["t"]][pos]
+        if w.kv_kind == "fp8":
+            cache = oracle.quant.Fp8Cache(oracle.quant.quantize_k_cache(bits))
+        else:
+            cache = oracle.quant.Bf16Cache(bits)
+        local = np.full_like(slots, -1)
+        local[0, :len(pos)] = np.arange(len(pos))
+        oracle.sparse_mla.sparse_mla(pr["q"], cache, local, w.sm_scale)
+    dt = time.perf_counter() - t0
+    return dict(value=len(per_row) / dt, unit="query-tokens/s", cores=int(cores),
+                kind="oracle",
+                sample=(f"{len(per_row)} of {w.num_rows} query rows of the same "
+                        f"workload (rows {per_row[0]['t']}..{per_row[-1]['t']}), "
+                        f"{dt:.1f} s; numpy fp64, batch metadata included"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus "
+              f"{args.gpus}); each GPU would run its own share of requests "
+              "with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sparse_attention_decode_indexer_amd as nsa
+    import workloads as W
+
+    nsa.load()
+    dev = torch.device("cuda:0")
+    w = W.make_workload(args.workload, device=dev, seed=args.seed)
+    fp8_kv = w.kv_kind == "fp8"
+    cache = nsa.nsa_quantize_k_cache(w.kv_bf16) if fp8_kv else w.kv_bf16
+    kvd = nsa.KV_FP8_656 if fp8_kv else nsa.KV_BF16_576
+    T = w.num_rows
+    idt = nsa.DTYPE_FP8_E4M3 if w.idx_kind == "fp8" else nsa.DTYPE_FP32
+    ncols = (w.max_seqlen_k + 63) // 64
+
+    # preallocated outputs (the library never allocates)
+    i32 = torch.int32
+    logits = torch.empty(T, w.max_seqlen_k, dtype=torch.float32, device=dev)
+    slots = torch.empty(T, w.topk, dtype=i32, device=dev)
+    out = torch.empty(T, w.heads, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(T, w.heads, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(nsa.sparse_mla_workspace_size(T, w.heads, w.topk), 16),
+                     dtype=torch.uint8, device=dev)
+    attn = nsa.nsa_sparse_mla_extend if w.mode == W.MODE_EXTEND else nsa.nsa_sparse_mla_decode
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+          for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        md = nsa.nsa_build_metadata(w.mode, w.seq_lens, w.req_to_token,
+                                    w.req_pool_indices, w.topk, w.max_seqlen_k, T,
+                                    extend_lens=w.extend_lens, draft_token_num=w.draft)
+        if e: e[1].record()
+        nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
+                               md["real_page_table"], md["token_to_req"],
+                               md["seqlens_expanded"], w.max_seqlen_k,
+                               logits=logits, dtype=idt)
+        if e: e[2].record()
+        nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
+                               w.max_seqlen_k, table=md["real_page_table"],
+                               token_to_req=md["token_to_req"], out=slots)
+        if e: e[3].record()
+        attn(w.q, cache, kvd, slots, w.sm_scale, md["nsa_cache_seqlens"],
+             out=out, lse=lse, workspace=ws)
+        if e: e[4].record()
+        return md
+
+    for _ in range(args.warmup):
+        step()
+    if args.copy_calibration:
+        src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        del src_c, dst_c
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        md = step(ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(4)]
+                      for k in range(args.steps)])          # ms
+    stage_ms = stage.mean(axis=0)
+    ms_per_step = elapsed * 1e3 / args.steps
+    se = md["seqlens_expanded"].cpu().numpy()     # visible length of every row
+    idx_bytes = indexer_bytes(se, w.idx_heads, w.idx_dim)
+    idx_ms = stage_ms[1]
+    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    pipe = pipeline_bytes(se, w.topk, w.heads, 656 if fp8_kv else 1152,
+                          w.idx_heads, w.idx_dim)
+    pipe_gbps = pipe / (ms_per_step * 1e-3) / 1e9
+    src = open(os.path.join(ROOT, "sparse_attention_decode_indexer_amd", "csrc",
+                            "indexer.hip"), "rb").read()
+    traffic = read_pmc(hashlib.sha256(src).hexdigest())
+
+    res = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (indexer, KV cache) / bf16 MFMA + fp32 softmax (MLA)",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": args.workload, "batch": w.bs, "query_rows": T,
+                   "max_seqlen_k": w.max_seqlen_k, "topk": w.topk,
+                   "mla_heads": w.heads, "kv_cache": w.kv_kind,
+                   "indexer": f"{w.idx_heads}x{w.idx_dim} {w.idx_kind}",
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "indexer_fp8_kernel", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": idx_bytes},
+        "pipeline": {"algorithmic_bytes_per_step": pipe, "GBps": pipe_gbps,
+                     "hbm_roofline_frac": pipe_gbps / HBM_PEAK_GBPS},
+        "stages_ms": {"metadata": stage_ms[0], "indexer": stage_ms[1],
+                      "topk_transform": stage_ms[2], "sparse_mla": stage_ms[3]},
+        "cpu_baseline": None,
+    }
+    if args.cpu_rows > 0:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -158,10 +158,13 @@ extern "C" int nsa_build_metadata(
     NSA_REQUIRE(extend_lens != nullptr, NSA_ERR_INVALID_ARG,
                 "%s: extend needs extend_lens", fn);
   }
-  NSA_REQUIRE(cache_seqlens && cu_seqlens_k && cu_seqlens_q &&
-                  seqlens_expanded && nsa_cache_seqlens && nsa_cu_seqlens_k &&
-                  nsa_cu_seqlens_q && real_page_table && token_to_req,
-              NSA_ERR_INVALID_ARG, "%s: null output pointer", fn);
+  // buffers of zero length may be NULL (an empty batch has no rows)
+  NSA_REQUIRE(cu_seqlens_k && cu_seqlens_q && nsa_cu_seqlens_k && nsa_cu_seqlens_q,
+              NSA_ERR_INVALID_ARG, "%s: null cumulative-length output", fn);
+  NSA_REQUIRE(bs == 0 || (cache_seqlens && (real_page_table || max_seqlen_k == 0)),
+              NSA_ERR_INVALID_ARG, "%s: null per-request output", fn);
+  NSA_REQUIRE(num_q_rows == 0 || (seqlens_expanded && nsa_cache_seqlens && token_to_req),
+              NSA_ERR_INVALID_ARG, "%s: null per-row output", fn);
   NSA_REQUIRE(bs == 0 || (seq_lens && req_to_token && req_pool_indices),
               NSA_ERR_INVALID_ARG, "%s: null input pointer", fn);
   const int64_t ncols = (max_seqlen_k + NSA_PAGE_SIZE - 1) / NSA_PAGE_SIZE;
