@@ -183,7 +183,8 @@ def main():
 
     # preallocated outputs (the library never allocates)
     i32 = torch.int32
-    logits = torch.empty(T, w.max_seqlen_k, dtype=torch.float32, device=dev)
+    logits = torch.empty(T, nsa.logits_row_stride(w.max_seqlen_k),
+                         dtype=torch.float32, device=dev)
     slots = torch.empty(T, w.topk, dtype=i32, device=dev)
     out = torch.empty(T, w.heads, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(T, w.heads, dtype=torch.float32, device=dev)
@@ -217,9 +218,12 @@ def main():
     for _ in range(args.warmup):
         step()
     if args.copy_calibration:
-        src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst_c = torch.empty_like(src_c)
+        # an elementwise int32 -> fp32 kernel over 1 GiB: reads 1 GiB, writes 1 GiB
+        src_c = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        dst_c = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
         dst_c.copy_(src_c)
+        torch.cuda.synchronize()
         del src_c, dst_c
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -146,6 +146,9 @@ int nsa_build_metadata(int mode, int bs, int draft_token_num, int topk,
  *                    [0, num_pages) yields -inf logits for its 64 positions.
  *   token_to_req[T], seqlens_expanded[T]  from nsa_build_metadata.
  *   logits           [T, logits_stride] fp32, logits_stride >= max_seqlen_k.
+ *                    Rows that start 256-byte aligned (stride a multiple of
+ *                    64) give whole-line stores here and vector loads in
+ *                    nsa_topk_transform; any stride is correct.
  * Supported: (fp8, Hi = 64, Di = 128) on the MFMA path; (fp32, Hi <= 64,
  * Di <= 128, Di % 4 == 0). page_size must be 64.
  */

@@ -86,6 +86,13 @@ def nsa_build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
     return out
 
 
+def logits_row_stride(max_seqlen_k):
+    """Row stride (elements) for a logits buffer: max_seqlen_k rounded up to a
+    multiple of 64 so every row starts 256-byte aligned (vector loads in
+    top-k, whole-line stores in the indexer)."""
+    return max(64, (max_seqlen_k + 63) // 64 * 64)
+
+
 def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits=None,
                        dtype=DTYPE_FP8_E4M3):
@@ -100,8 +107,8 @@ def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
     _check(seqlens_expanded, "seqlens_expanded", torch.int32, 1)
     T, Hi, Di = q.shape
     if logits is None:
-        logits = torch.empty(T, max(max_seqlen_k, 1), dtype=torch.float32,
-                             device=q.device)
+        logits = torch.empty(T, logits_row_stride(max_seqlen_k),
+                             dtype=torch.float32, device=q.device)
     _check(logits, "logits", torch.float32, 2, contiguous=False)
     call("nsa_indexer_logits", _ptr(q), dtype, _ptr(weights), _ptr(index_cache),
          dtype, index_cache.shape[0], _ptr(real_page_table),

@@ -35,7 +35,7 @@ constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kPageBytesFp8 = kPage * kDim + kPage * 4;  // 8448
 constexpr int kWaves = 4;
-constexpr int kPagesPerBlock = 32;
+constexpr int kPagesPerBlock = 64;
 
 // Logical block id such that consecutive ids run on the same XCD (work
 // groups are dealt to the 8 XCDs round-robin).
@@ -104,27 +104,26 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
   const int32_t* prow = rpt + (int64_t)t2r[t] * rpt_stride;
   float* lrow = logits + t * logits_stride;
 
-  int p = p_begin + wave;
-  if (p >= p_end) return;
-  int page = __builtin_amdgcn_readfirstlane(prow[p]);
-  bool ok = page >= 0 && page < num_pages;
-  PageKeys cur;
-  if (ok) load_page(cur, cache + (int64_t)page * kPageBytesFp8, c, g);
+  // this wave's pages: p_begin + wave + 4 i, i < np_w (at most 16); lane i
+  // holds the id of the i-th one, so no key load waits on an id load
+  const int first = p_begin + wave;
+  if (first >= p_end) return;
+  const int np_w = (p_end - first + kWaves - 1) / kWaves;
+  const int id_lane = lane < np_w ? prow[first + kWaves * lane] : -1;
 
-  while (true) {
-    const int pn = p + kWaves;
-    int page_n = 0;
-    bool ok_n = false;
-    PageKeys nxt;
-    if (pn < p_end) {
-      page_n = __builtin_amdgcn_readfirstlane(prow[pn]);
-      ok_n = page_n >= 0 && page_n < num_pages;
-      if (ok_n) load_page(nxt, cache + (int64_t)page_n * kPageBytesFp8, c, g);
-    }
-
+  auto page_id = [&](int i) -> int {
+    const int id = __builtin_amdgcn_readlane(id_lane, i);
+    return (id >= 0 && id < num_pages) ? id : -1;
+  };
+  auto fetch = [&](PageKeys& pk, int i) {
+    const int id = page_id(i);
+    if (id >= 0) load_page(pk, cache + (int64_t)id * kPageBytesFp8, c, g);
+  };
+  auto score = [&](const PageKeys& pk, int i) {
+    const int id = page_id(i);
     float result = -INFINITY;
-    if (ok) {
-      const uint8_t* base = cache + (int64_t)page * kPageBytesFp8;
+    if (id >= 0) {
+      const uint8_t* base = cache + (int64_t)id * kPageBytesFp8;
       const float ks = *reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane);
       float v[4];
 #pragma unroll
@@ -133,7 +132,7 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
           const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qa[ht], cur.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+              qa[ht], pk.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) s = fmaf(wr[ht][r], fmaxf(acc[r], 0.0f), s);
         }
@@ -144,16 +143,26 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
       const float u0 = (b0 ? v[1] : v[0]) + __shfl_xor(b0 ? v[0] : v[1], 16);
       const float u1 = (b0 ? v[3] : v[2]) + __shfl_xor(b0 ? v[2] : v[3], 16);
       const float tot = (b1 ? u1 : u0) + __shfl_xor(b1 ? u0 : u1, 32);
-      result = tot * ks;  // token p*64 + lane
+      result = tot * ks;  // position (first + 4 i) * 64 + lane
     }
-    const int s = p * kPage + lane;
+    const int s = (first + kWaves * i) * kPage + lane;
     if (s < L) lrow[s] = result;
+  };
 
-    if (pn >= p_end) break;
-    p = pn;
-    page = page_n;
-    ok = ok_n;
-    cur = nxt;
+  // three page buffers: keys of pages i+1 and i+2 are in flight while page i
+  // is scored
+  PageKeys b0, b1, b2;
+  fetch(b0, 0);
+  if (1 < np_w) fetch(b1, 1);
+  for (int i = 0; i < np_w; i += 3) {
+    if (i + 2 < np_w) fetch(b2, i + 2);
+    score(b0, i);
+    if (i + 1 >= np_w) break;
+    if (i + 3 < np_w) fetch(b0, i + 3);
+    score(b1, i + 1);
+    if (i + 2 >= np_w) break;
+    if (i + 4 < np_w) fetch(b1, i + 4);
+    score(b2, i + 2);
   }
 }
 

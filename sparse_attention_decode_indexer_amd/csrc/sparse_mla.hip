@@ -8,18 +8,23 @@
 //   lse = log sum_i exp(s_i).
 //
 // MI355X design (one 256-thread block = 4 waves):
-//   * a block owns one query row, HB = 16*HW heads and one KV split; wave w
-//     owns head tile w % HW and dim slice w / HW of DW = 4 / HW slices (so
-//     16-head models use all 4 waves by splitting the 576 contraction dims
-//     in QK and the 512 value dims in PV);
+//   * a block owns one query row, HB = 16*NH*HW heads and one KV split; wave
+//     w owns NH head tiles of 16 (tile w % HW) and dim slice w / HW of
+//     DW = 4 / HW slices (16-head models use all 4 waves by splitting the 576
+//     contraction dims in QK and the 512 value dims in PV);
 //   * per step, 32 selected slots are gathered with 16-byte loads (issued
 //     one step ahead), dequantised to bf16 if the cache is fp8, and staged
-//     in LDS twice: row-major for Q.K (A operand = keys, 16 slots x 32 dims
-//     per v_mfma_f32_16x16x32_bf16) and transposed for P.V (B operand = 8
-//     slots of one value dim);
-//   * S^T = K.Q^T puts one head per lane column, so P is already in the A
-//     layout of P.V (heads x slots) and needs no shuffles; the online
-//     softmax runs in the log2 domain in fp32;
+//     once in LDS, row-major;
+//   * S^T = K.Q^T (v_mfma_f32_16x16x32_bf16, A = 16 slots x 32 dims read
+//     from LDS, B = Q^T held in registers) puts one head per lane column, so
+//     P is already in the A layout of P.V (heads x slots) and needs no
+//     shuffles; each A fragment feeds NH MFMAs;
+//   * P.V reads its B operand (8 slots of one value dim per lane) from the
+//     same row-major tile with ds_read_b64_tr_b16: within each 16-lane group,
+//     source lane s points at 4 dims of slot row s/4 and the hardware
+//     transposes, giving lane i dim i of 4 slot rows; each B fragment feeds
+//     NH MFMAs;
+//   * the online softmax runs in the log2 domain in fp32;
 //   * KV splits write (o / l, lse) partials to the workspace and a second
 //     kernel merges them in split order (bit-reproducible).
 #include "common.h"
@@ -30,12 +35,12 @@ constexpr int kThreads = 256;
 constexpr int kStep = 32;                 // slots per step
 constexpr int kDQK = 576, kDV = 512;
 constexpr int kKsStride = kDQK + 8;       // bf16 elements per staged K row
-constexpr int kVtStride = kStep + 4;      // bf16 elements per staged V^T row
-constexpr int kKsBytes = kStep * kKsStride * 2;   // 37376
-constexpr int kVtBytes = kDV * kVtStride * 2;     // 36864
+constexpr int kKsRow = kKsStride * 2;     // bytes per staged K row (1168)
+constexpr int kKsBytes = kStep * kKsRow;  // 37376
 constexpr int kKSteps = kDQK / 32;        // 18 contraction steps of 32 dims
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;             // log2 headroom before O is rescaled
 
 struct Params {
   const uint16_t* q;
@@ -59,17 +64,25 @@ __device__ __forceinline__ uint32_t xcd_logical_block(uint32_t bid, uint32_t n) 
   return x * q + (x < r ? x : r) + bid / 8;
 }
 
-// bf16 pair selection: lo halves of a and b -> (a.lo, b.lo); hi halves.
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 4 bf16 of one value dim across 4 slot rows (see the design note above).
+__device__ __forceinline__ v4i16 read_tr(const uint8_t* lds_byte_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(__attribute__((address_space(3))) uint8_t*)lds_byte_addr);
 }
 
-// Prefetch registers of one thread for one step.
+// Prefetch registers of one thread for one step. Loads are branch-free: an
+// absent slot (-1) reads slot 0 and its values are zeroed when staged, so no
+// load sits behind a branch (a branch around a load makes the compiler wait
+// for every load in flight).
 template <bool FP8>
 struct Stage;
+
+__device__ __forceinline__ uint4 keep_if(bool v, uint4 x) {
+  return v ? x : make_uint4(0, 0, 0, 0);
+}
 
 // bf16 cache: two (4 slots x 8 dims) pieces of the value part + one rope
 // piece of 8 dims.
@@ -77,8 +90,10 @@ template <>
 struct Stage<false> {
   uint4 v[2][4];
   uint4 rope;
+  uint32_t valid;   // bit 4*it+s: slot s of piece it; bit 8: rope slot
   __device__ __forceinline__ void load(const Params& p, const int32_t* ids,
                                        int tid) {
+    valid = 0;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int item = tid + it * kThreads;
@@ -86,41 +101,28 @@ struct Stage<false> {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int32_t slot = ids[qd * 4 + s];
-        if (slot >= 0)
-          v[it][s] = *reinterpret_cast<const uint4*>(
-              p.kv + (int64_t)slot * (kDQK * 2) + ch * 16);
-        else
-          v[it][s] = make_uint4(0, 0, 0, 0);
+        valid |= (slot >= 0 ? 1u : 0u) << (4 * it + s);
+        v[it][s] = *reinterpret_cast<const uint4*>(
+            p.kv + (int64_t)(slot >= 0 ? slot : 0) * (kDQK * 2) + ch * 16);
       }
     }
     const int32_t slot = ids[tid >> 3];
-    rope = slot >= 0 ? *reinterpret_cast<const uint4*>(
-                           p.kv + (int64_t)slot * (kDQK * 2) + kDV * 2 + (tid & 7) * 16)
-                     : make_uint4(0, 0, 0, 0);
+    valid |= (slot >= 0 ? 1u : 0u) << 8;
+    rope = *reinterpret_cast<const uint4*>(
+        p.kv + (int64_t)(slot >= 0 ? slot : 0) * (kDQK * 2) + kDV * 2 + (tid & 7) * 16);
   }
-  __device__ __forceinline__ void store(uint8_t* ks, uint8_t* vt, int tid) const {
+  __device__ __forceinline__ void store(uint8_t* ks, float*, int tid) const {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int item = tid + it * kThreads;
       const int qd = item >> 6, ch = item & 63;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        *reinterpret_cast<uint4*>(ks + (qd * 4 + s) * (kKsStride * 2) + ch * 16) = v[it][s];
-      // transpose 4 slots x 8 dims -> 8 dims x 4 slots
-      const uint32_t a[4] = {v[it][0].x, v[it][0].y, v[it][0].z, v[it][0].w};
-      const uint32_t b[4] = {v[it][1].x, v[it][1].y, v[it][1].z, v[it][1].w};
-      const uint32_t c[4] = {v[it][2].x, v[it][2].y, v[it][2].z, v[it][2].w};
-      const uint32_t d[4] = {v[it][3].x, v[it][3].y, v[it][3].z, v[it][3].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dim = ch * 8 + 2 * e;
-        uint2 w0 = make_uint2(lo_pair(a[e], b[e]), lo_pair(c[e], d[e]));
-        uint2 w1 = make_uint2(hi_pair(a[e], b[e]), hi_pair(c[e], d[e]));
-        *reinterpret_cast<uint2*>(vt + dim * (kVtStride * 2) + qd * 8) = w0;
-        *reinterpret_cast<uint2*>(vt + (dim + 1) * (kVtStride * 2) + qd * 8) = w1;
-      }
+        *reinterpret_cast<uint4*>(ks + (qd * 4 + s) * kKsRow + ch * 16) =
+            keep_if((valid >> (4 * it + s)) & 1u, v[it][s]);
     }
-    *reinterpret_cast<uint4*>(ks + (tid >> 3) * (kKsStride * 2) + kDV * 2 + (tid & 7) * 16) = rope;
+    *reinterpret_cast<uint4*>(ks + (tid >> 3) * kKsRow + kDV * 2 + (tid & 7) * 16) =
+        keep_if((valid >> 8) & 1u, rope);
   }
 };
 
@@ -131,65 +133,63 @@ struct Stage<true> {
   uint4 code[4];
   float scale[4];
   uint4 rope;
+  uint32_t valid;   // bit s: slot s of the piece; bit 4: rope slot
   __device__ __forceinline__ void load(const Params& p, const int32_t* ids,
                                        int tid) {
     const int qd = tid >> 5, cc = tid & 31;
+    valid = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int32_t slot = ids[qd * 4 + s];
-      if (slot >= 0) {
-        const uint8_t* row = p.kv + (int64_t)slot * 656;
-        code[s] = *reinterpret_cast<const uint4*>(row + cc * 16);
-        scale[s] = *reinterpret_cast<const float*>(row + 512 + 4 * (cc >> 3));
-      } else {
-        code[s] = make_uint4(0, 0, 0, 0);
-        scale[s] = 0.0f;
-      }
+      valid |= (slot >= 0 ? 1u : 0u) << s;
+      const uint8_t* row = p.kv + (int64_t)(slot >= 0 ? slot : 0) * 656;
+      code[s] = *reinterpret_cast<const uint4*>(row + cc * 16);
+      scale[s] = *reinterpret_cast<const float*>(row + 512 + 4 * (cc >> 3));
     }
     const int32_t slot = ids[tid >> 3];
-    rope = slot >= 0 ? *reinterpret_cast<const uint4*>(p.kv + (int64_t)slot * 656 +
-                                                       528 + (tid & 7) * 16)
-                     : make_uint4(0, 0, 0, 0);
+    valid |= (slot >= 0 ? 1u : 0u) << 4;
+    rope = *reinterpret_cast<const uint4*>(p.kv + (int64_t)(slot >= 0 ? slot : 0) * 656 +
+                                           528 + (tid & 7) * 16);
   }
-  __device__ __forceinline__ void store(uint8_t* ks, uint8_t* vt, int tid) const {
+  // codes are converted exactly (every e4m3 value is a bf16 value: the fp32
+  // image has 16 zero low bits, so the upper halves are taken); the block
+  // scales go to LDS and are applied to the scores and to P
+  __device__ __forceinline__ void store(uint8_t* ks, float* scl, int tid) const {
     const int qd = tid >> 5, cc = tid & 31;
-    uint32_t bf[4][8];  // [slot][dim pair]: 16 dims as 8 bf16 pairs
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t w[4] = {code[s].x, code[s].y, code[s].z, code[s].w};
+      const bool ok = (valid >> s) & 1u;
+      const uint4 cs = keep_if(ok, code[s]);
+      const uint32_t w[4] = {cs.x, cs.y, cs.z, cs.w};
+      uint32_t bf[8];  // 16 dims as 8 bf16 pairs
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
         const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-        bf[s][2 * i] = pack_bf16x2(lo[0] * scale[s], lo[1] * scale[s]);
-        bf[s][2 * i + 1] = pack_bf16x2(hi[0] * scale[s], hi[1] * scale[s]);
+        bf[2 * i] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+        bf[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
       }
-      uint8_t* dst = ks + (qd * 4 + s) * (kKsStride * 2) + cc * 32;
-      *reinterpret_cast<uint4*>(dst) = make_uint4(bf[s][0], bf[s][1], bf[s][2], bf[s][3]);
-      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(bf[s][4], bf[s][5], bf[s][6], bf[s][7]);
+      uint8_t* dst = ks + (qd * 4 + s) * kKsRow + cc * 32;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(bf[0], bf[1], bf[2], bf[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(bf[4], bf[5], bf[6], bf[7]);
+      if ((cc & 7) == 0) scl[(qd * 4 + s) * 4 + (cc >> 3)] = ok ? scale[s] : 0.0f;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dim = cc * 16 + 2 * e;
-      uint2 w0 = make_uint2(lo_pair(bf[0][e], bf[1][e]), lo_pair(bf[2][e], bf[3][e]));
-      uint2 w1 = make_uint2(hi_pair(bf[0][e], bf[1][e]), hi_pair(bf[2][e], bf[3][e]));
-      *reinterpret_cast<uint2*>(vt + dim * (kVtStride * 2) + qd * 8) = w0;
-      *reinterpret_cast<uint2*>(vt + (dim + 1) * (kVtStride * 2) + qd * 8) = w1;
-    }
-    *reinterpret_cast<uint4*>(ks + (tid >> 3) * (kKsStride * 2) + kDV * 2 + (tid & 7) * 16) = rope;
+    *reinterpret_cast<uint4*>(ks + (tid >> 3) * kKsRow + kDV * 2 + (tid & 7) * 16) =
+        keep_if((valid >> 4) & 1u, rope);
   }
 };
 
-template <int HW, bool FP8>
-__global__ void __launch_bounds__(kThreads, (HW == 4 ? 1 : 2))
+template <int NH, int HW, bool FP8>
+__global__ void __launch_bounds__(kThreads, 2)
 sparse_mla_kernel(const Params p) {
   constexpr int DW = 4 / HW;                 // dim slices
   constexpr int KSW = (kKSteps + DW - 1) / DW;
   constexpr int NT = kDV / DW / 16;          // value-dim tiles per wave
   __shared__ __attribute__((aligned(16))) uint8_t ks[kKsBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kVtBytes];
-  __shared__ int32_t ids[2][kStep];
-  __shared__ uint32_t vmask[2];
+  __shared__ float red[DW > 1 ? 4 * 2 * 4 * 64 : 1];   // partial scores
+  __shared__ float scl[FP8 ? kStep * 4 : 1];            // block scales of the step
+  __shared__ int32_t ids[4][kStep];     // ring: slot ids of steps s..s+3
+  __shared__ uint32_t vmask[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -200,9 +200,9 @@ sparse_mla_kernel(const Params p) {
   const int hb = lb % p.n_hb;
   const int split = (lb / p.n_hb) % p.n_splits;
   const int64_t t = lb / (p.n_hb * p.n_splits);
-  const int h0 = hb * (16 * HW) + hw * 16;   // first head of this wave
+  const int h0 = hb * (16 * NH * HW) + hw * (16 * NH);   // first head of this wave
 
-  int n_row = p.topk;
+  int n_row = p.num_slots > 0 ? p.topk : 0;   // no cache rows: every row is empty
   if (p.seqlens) {
     const int sl = p.seqlens[t];
     n_row = sl < 0 ? 0 : (sl < n_row ? sl : n_row);
@@ -212,30 +212,33 @@ sparse_mla_kernel(const Params p) {
   const int nsteps = s_end > s_begin ? (s_end - s_begin + kStep - 1) / kStep : 0;
   const int32_t* irow = p.idx + t * p.idx_stride;
 
-  // Q as the B operand of S^T = K.Q^T: lane (head c, group g) holds dims
-  // ks*32 + 8g .. +8 of its head for the wave's contraction steps
-  bf16x8 qb[KSW];
-  {
-    const uint16_t* qh = p.q + t * p.q_tok_stride + (int64_t)(h0 + c) * p.q_head_stride;
+  // Q as the B operand of S^T = K.Q^T: lane (head c of tile nh, group g)
+  // holds dims ks*32 + 8g .. +8 for the wave's contraction steps
+  bf16x8 qb[NH][KSW];
+#pragma unroll
+  for (int nh = 0; nh < NH; ++nh) {
+    const uint16_t* qh = p.q + t * p.q_tok_stride +
+                         (int64_t)(h0 + nh * 16 + c) * p.q_head_stride;
 #pragma unroll
     for (int i = 0; i < KSW; ++i) {
       const int kstep = dw + DW * i;
       if (kstep < kKSteps)
-        qb[i] = *reinterpret_cast<const bf16x8*>(qh + kstep * 32 + g * 8);
+        qb[nh][i] = *reinterpret_cast<const bf16x8*>(qh + kstep * 32 + g * 8);
     }
   }
 
+  // Slot ids are loaded a few steps ahead and only checked when published:
+  // using a loaded value right away would make the wave wait for every
+  // memory load in flight, including the gather of the next steps.
   auto load_ids = [&](int step) -> int32_t {
-    // thread j < 32: id of slot j of `step` (-1 when absent or invalid)
+    // thread j < 32: raw id of slot j of `step` (-1 past the row's end)
     const int pos = s_begin + step * kStep + tid;
-    int32_t id = -1;
-    if (tid < kStep && step < nsteps && pos < s_end) {
-      id = irow[pos];
-      if (id < 0 || id >= p.num_slots) id = -1;
-    }
-    return id;
+    const bool in = tid < kStep && step < nsteps && pos < s_end;
+    const int32_t id = irow[in ? pos : s_begin];
+    return in ? id : -1;
   };
   auto publish_ids = [&](int buf, int32_t id) {
+    if (id < 0 || id >= p.num_slots) id = -1;
     if (tid < kStep) ids[buf][tid] = id;
     if (wave == 0) {
       const unsigned long long b = __ballot(tid < kStep && id >= 0);
@@ -243,29 +246,47 @@ sparse_mla_kernel(const Params p) {
     }
   };
 
-  f32x4 o[NT];
+  f32x4 o[NH][NT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.0f;
+  for (int nh = 0; nh < NH; ++nh)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) o[nh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // m: reference max (log2 domain) of each head, raised only when a step's
+  // max exceeds it by more than kLazy, so O is rarely rescaled
+  float m[NH], l[NH];
+#pragma unroll
+  for (int nh = 0; nh < NH; ++nh) { m[nh] = -INFINITY; l[nh] = 0.0f; }
 
-  Stage<FP8> st;
+  // the rows of step i+1 are loaded while step i is computed
+  Stage<FP8> sa;
   if (nsteps > 0) {
     publish_ids(0, load_ids(0));
     publish_ids(1, load_ids(1));
+    publish_ids(2, load_ids(2));
     __syncthreads();
-    st.load(p, ids[0], tid);
-    st.store(ks, vt, tid);
+    sa.load(p, ids[0], tid);
+    sa.store(ks, scl, tid);
+
     __syncthreads();
   }
-  int32_t id_ahead = load_ids(2);
+  int32_t id_ahead = load_ids(3);
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) st.load(p, ids[buf ^ 1], tid);   // next step's slots
+  auto run_step = [&](int step) {
+    const int buf = step & 3;
+    Stage<FP8> nx;
+    if (step + 1 < nsteps) nx.load(p, ids[(step + 1) & 3], tid);
 
-    // ---- S^T = K . Q^T (partial over this wave's contraction steps)
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // ---- S^T = K . Q^T (partial over this wave's contraction steps). For an
+    // fp8 cache each 128-dim block is accumulated apart and scaled by its
+    // slot's block scale; rope dims are unscaled.
+    f32x4 acc[2][NH], tmp[2][NH];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nh = 0; nh < NH; ++nh) {
+        acc[mt][nh] = f32x4{0.f, 0.f, 0.f, 0.f};
+        tmp[mt][nh] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
     for (int i = 0; i < KSW; ++i) {
       const int kstep = dw + DW * i;
@@ -273,125 +294,194 @@ sparse_mla_kernel(const Params p) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              ks + (mt * 16 + c) * (kKsStride * 2) + (kstep * 32 + g * 8) * 2);
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[i], acc[mt], 0, 0, 0);
+              ks + (mt * 16 + c) * kKsRow + (kstep * 32 + g * 8) * 2);
+#pragma unroll
+          for (int nh = 0; nh < NH; ++nh)
+            tmp[mt][nh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[nh][i], tmp[mt][nh], 0, 0, 0);
+        }
+        if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        const int blk = kstep < 16 ? kstep >> 2 : 4;
+        const int nk = kstep + DW;
+        const int nblk = nk < kKSteps ? (nk < 16 ? nk >> 2 : 4) : -1;
+        if (nblk != blk) {   // flush the block's partial scores
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float sc = 1.0f;
+              if constexpr (FP8) {
+                if (blk < 4) sc = scl[(mt * 16 + 4 * g + r) * 4 + blk];
+              }
+#pragma unroll
+              for (int nh = 0; nh < NH; ++nh) {
+                acc[mt][nh][r] = fmaf(sc, tmp[mt][nh][r], acc[mt][nh][r]);
+                tmp[mt][nh][r] = 0.0f;
+              }
+            }
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (DW > 1) {
       // sum the DW partial scores of this head tile, in slice order
-      float* red = reinterpret_cast<float*>(ks);
-      __syncthreads();  // every wave has finished reading ks
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[((wave * 2 + mt) * 4 + r) * 64 + lane] = acc[mt][r];
+        for (int r = 0; r < 4; ++r) red[((wave * 2 + mt) * 4 + r) * 64 + lane] = acc[mt][0][r];
       __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float s = 0.0f;
+          float sum = 0.0f;
 #pragma unroll
           for (int j = 0; j < DW; ++j)
-            s += red[(((j * HW + hw) * 2 + mt) * 4 + r) * 64 + lane];
-          acc[mt][r] = s;
+            sum += red[(((j * HW + hw) * 2 + mt) * 4 + r) * 64 + lane];
+          acc[mt][0][r] = sum;
         }
     }
 
-    // ---- online softmax: lane (head c, group g) holds slots mt*16+4g+r
+    // ---- online softmax with a lazily raised reference max: lane (head c,
+    // group g) holds slots mt*16+4g+r. In the common step no lane crosses
+    // its head's reference max by more than kLazy, nothing is exchanged
+    // between lanes and O keeps its scale; l is kept per lane and summed
+    // across the head's lanes at the end.
     const uint32_t valid = vmask[buf];
-    float sv[2][4];
-    float mx = -INFINITY;
+    float pv[NH][2][4];
+    float al[NH][4];
+    bool need = false;
+    float lmx[NH];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int nh = 0; nh < NH; ++nh) {
+      lmx[nh] = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = mt * 16 + 4 * g + r;
-        sv[mt][r] = ((valid >> j) & 1u) ? acc[mt][r] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[mt][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = exp2f(m - m_use);
-    float psum = 0.0f;
-    uint32_t pw[4];
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      float pr[4];
+        for (int r = 0; r < 4; ++r) {
+          const int j = mt * 16 + 4 * g + r;
+          pv[nh][mt][r] = ((valid >> j) & 1u) ? acc[mt][nh][r] * p.scale_log2 : -INFINITY;
+          lmx[nh] = fmaxf(lmx[nh], pv[nh][mt][r]);
+        }
+      need = need || lmx[nh] > m[nh] + kLazy;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[r] = exp2f(sv[mt][r] - m_use);
-        psum += pr[r];
-      }
-      pw[mt * 2] = pack_bf16x2(pr[0], pr[1]);
-      pw[mt * 2 + 1] = pack_bf16x2(pr[2], pr[3]);
+      for (int r = 0; r < 4; ++r) al[nh][r] = 1.0f;
     }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l = l * alpha + psum;
-    m = m_new;
-    bf16x8 pa;
-    {
-      const uint4 u = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-      pa = *reinterpret_cast<const bf16x8*>(&u);
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      // rare: agree on each head's new reference max and rescale
+#pragma unroll
+      for (int nh = 0; nh < NH; ++nh) {
+        float mx = lmx[nh];
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool upd = mx > m[nh] + kLazy;   // same in the head's 4 lanes
+        const float alpha = upd ? exp2f(m[nh] - mx) : 1.0f;   // m = -inf -> 0
+        if (upd) m[nh] = mx;
+        l[nh] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) al[nh][r] = __shfl(alpha, 4 * g + r);
+      }
+    }
+#pragma unroll
+    for (int nh = 0; nh < NH; ++nh) {
+      const float m_use = m[nh] == -INFINITY ? 0.0f : m[nh];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[nh][mt][r] = exp2f(pv[nh][mt][r] - m_use);
+          l[nh] += pv[nh][mt][r];
+        }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[nh][nt][r] *= al[nh][r];
     }
 
-    // ---- rescale O rows (heads 4g + r) and accumulate P . V
-    float al[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r);
+    // ---- P . V: the B operand (slots 4g..4g+3 and 16+4g..16+4g+3 of value
+    // dim `dim`) comes from two transposing reads of the row-major tile; for
+    // an fp8 cache P carries the slot's scale of the value dims' block
+    bf16x8 pa[NH];
+    int pa_blk = -1;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      const int n0 = dw * (kDV / DW) + nt * 16;
+      const int blk = n0 >> 7;
+      if (blk != pa_blk) {
+        pa_blk = blk;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
-      const int dim = dw * (kDV / DW) + nt * 16 + c;
-      const uint8_t* vrow = vt + dim * (kVtStride * 2);
-      const uint2 b0 = *reinterpret_cast<const uint2*>(vrow + g * 8);
-      const uint2 b1 = *reinterpret_cast<const uint2*>(vrow + 32 + g * 8);
-      const uint4 bu = make_uint4(b0.x, b0.y, b1.x, b1.y);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&bu);
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, b, o[nt], 0, 0, 0);
+        for (int nh = 0; nh < NH; ++nh) {
+          uint32_t pw[4];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            float q4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float sc = 1.0f;
+              if constexpr (FP8) sc = scl[(mt * 16 + 4 * g + r) * 4 + blk];
+              q4[r] = pv[nh][mt][r] * sc;
+            }
+            pw[mt * 2] = pack_bf16x2(q4[0], q4[1]);
+            pw[mt * 2 + 1] = pack_bf16x2(q4[2], q4[3]);
+          }
+          const uint4 u = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+          pa[nh] = *reinterpret_cast<const bf16x8*>(&u);
+        }
+      }
+      const uint8_t* src = ks + (4 * g + (c >> 2)) * kKsRow + (n0 + 4 * (c & 3)) * 2;
+      const v4i16 b0 = read_tr(src);
+      const v4i16 b1 = read_tr(src + 16 * kKsRow);
+      const v4i16 bb[2] = {b0, b1};
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(bb);
+#pragma unroll
+      for (int nh = 0; nh < NH; ++nh)
+        o[nh][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[nh], b, o[nh][nt], 0, 0, 0);
+      if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- stage the next step
-    __syncthreads();  // all waves are done with ks / vt / ids[buf]
-    if (more) st.store(ks, vt, tid);
-    publish_ids(buf, id_ahead);     // ids of step + 2
-    id_ahead = load_ids(step + 3);
+    // ---- stage step + 1 (its rows were issued a step ago)
+    __syncthreads();  // all waves are done with ks / ids[buf]
+    if (step + 1 < nsteps) nx.store(ks, scl, tid);
+    publish_ids((step + 3) & 3, id_ahead);
+    id_ahead = load_ids(step + 4);
     __syncthreads();
-  }
+  };
+
+  for (int step = 0; step < nsteps; ++step) run_step(step);
 
   // ---- finalize: lane (dim c of tile nt, group g) holds O[head 4g+r][dim]
-  float lr[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) lr[r] = __shfl(l, 4 * g + r);
-  const float lse_val = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-  if (p.n_splits == 1) {
+  for (int nh = 0; nh < NH; ++nh) {
+    l[nh] += __shfl_xor(l[nh], 16);
+    l[nh] += __shfl_xor(l[nh], 32);
+    float lr[4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int dim = dw * (kDV / DW) + nt * 16 + c;
+    for (int r = 0; r < 4; ++r) lr[r] = __shfl(l[nh], 4 * g + r);
+    const float lse_val = l[nh] > 0.0f ? (m[nh] + __log2f(l[nh])) * kLn2 : -INFINITY;
+    const int hbase = h0 + nh * 16;
+    if (p.n_splits == 1) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = lr[r] > 0.0f ? o[nt][r] / lr[r] : 0.0f;
-        p.out[(t * p.H + h0 + 4 * g + r) * kDV + dim] = (uint16_t)f32_to_bf16_bits(v);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int dim = dw * (kDV / DW) + nt * 16 + c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = lr[r] > 0.0f ? o[nh][nt][r] / lr[r] : 0.0f;
+          p.out[(t * p.H + hbase + 4 * g + r) * kDV + dim] = (uint16_t)f32_to_bf16_bits(v);
+        }
       }
-    }
-    if (p.lse && dw == 0 && g == 0) p.lse[t * p.H + h0 + c] = lse_val;
-  } else {
-    const int64_t base = ((int64_t)split * p.T + t) * p.H;
+      if (p.lse && dw == 0 && g == 0) p.lse[t * p.H + hbase + c] = lse_val;
+    } else {
+      const int64_t base = ((int64_t)split * p.T + t) * p.H;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int dim = dw * (kDV / DW) + nt * 16 + c;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int dim = dw * (kDV / DW) + nt * 16 + c;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = lr[r] > 0.0f ? o[nt][r] / lr[r] : 0.0f;
-        p.ws_o[(base + h0 + 4 * g + r) * kDV + dim] = v;
+        for (int r = 0; r < 4; ++r) {
+          const float v = lr[r] > 0.0f ? o[nh][nt][r] / lr[r] : 0.0f;
+          p.ws_o[(base + hbase + 4 * g + r) * kDV + dim] = v;
+        }
       }
+      if (dw == 0 && g == 0) p.ws_lse[base + hbase + c] = lse_val;
     }
-    if (dw == 0 && g == 0) p.ws_lse[base + h0 + c] = lse_val;
   }
 }
 
@@ -432,17 +522,19 @@ combine_splits_kernel(const float* __restrict__ ws_o,
 }
 
 struct Plan {
-  int hb_heads, n_hb, n_splits, split_slots;
+  int nh, hw, hb_heads, n_hb, n_splits, split_slots;
 };
 
 Plan make_plan(int T, int H, int topk, bool decode) {
   Plan pl;
-  pl.hb_heads = (H % 64 == 0) ? 64 : ((H % 32 == 0) ? 32 : 16);
+  if (H % 32 == 0) { pl.nh = 1; pl.hw = 2; }
+  else { pl.nh = 1; pl.hw = 1; }
+  pl.hb_heads = 16 * pl.nh * pl.hw;
   pl.n_hb = H / pl.hb_heads;
   const int64_t base = (int64_t)T * pl.n_hb;
   const int max_splits = (topk + 127) / 128;   // >= 128 slots per split
   int ns = 1;
-  const int64_t target = decode ? 512 : 256;
+  const int64_t target = decode ? 256 : 128;
   if (base < target) ns = (int)((target + base - 1) / base);
   ns = ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
   int ss = (topk + ns - 1) / ns;
@@ -527,16 +619,14 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = kv_dtype == NSA_KV_FP8_656;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (pl.hb_heads == 64) {
-    if (fp8) hipLaunchKernelGGL((sparse_mla_kernel<4, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((sparse_mla_kernel<4, false>), grid, block, 0, s, p);
-  } else if (pl.hb_heads == 32) {
-    if (fp8) hipLaunchKernelGGL((sparse_mla_kernel<2, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((sparse_mla_kernel<2, false>), grid, block, 0, s, p);
-  } else {
-    if (fp8) hipLaunchKernelGGL((sparse_mla_kernel<1, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((sparse_mla_kernel<1, false>), grid, block, 0, s, p);
-  }
+#define NSA_MLA_LAUNCH(NH, HW)                                                      \
+  do {                                                                            \
+    if (fp8) hipLaunchKernelGGL((sparse_mla_kernel<NH, HW, true>), grid, block, 0, s, p); \
+    else hipLaunchKernelGGL((sparse_mla_kernel<NH, HW, false>), grid, block, 0, s, p);    \
+  } while (0)
+  if (pl.hw == 2) NSA_MLA_LAUNCH(1, 2);
+  else NSA_MLA_LAUNCH(1, 1);
+#undef NSA_MLA_LAUNCH
   st = nsa::check_launch(fn);
   if (st != NSA_OK || pl.n_splits == 1) return st;
   const int64_t cb = ((int64_t)T * H + 3) / 4;

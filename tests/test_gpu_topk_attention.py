@@ -34,12 +34,14 @@ def _topk_rows(rng, lengths, width, kind):
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "const", "special"])
 @pytest.mark.parametrize("topk", [256, 2048])
-def test_topk_exact_on_given_logits(kind, topk):
+@pytest.mark.parametrize("pad", [6, 67])   # odd row stride: scalar loads; else vector
+def test_topk_exact_on_given_logits(kind, topk, pad):
     nsa = need_gpu()
-    note(f"topk exact {kind} topk={topk}")
+    note(f"topk exact {kind} topk={topk} pad={pad}")
     rng = np.random.default_rng(topk)
-    lengths = [0, 1, topk - 1, topk, topk + 1, 3 * topk + 5, 20000, 131072 - 3]
-    width = max(lengths) + 7
+    lengths = [0, 1, topk - 1, topk, topk + 1, 3 * topk + 5, 20000, 131072 - 3,
+               16384, 16385, 32768 + 11]
+    width = max(lengths) + pad
     x = _topk_rows(rng, lengths, width, kind)
     lg = torch.as_tensor(x, device=DEV)
     ln = torch.as_tensor(lengths, dtype=torch.int32, device=DEV)
