@@ -6,16 +6,21 @@
 // variant fast_topk_transform_fused returns physical slots through the page
 // table instead of logical positions.
 //
-// Method (MI355X design, one 1024-thread block per row):
-//   * rows with n <= topk keep 0..n-1 (no logits are read);
-//   * otherwise a radix select on the order-preserving uint32 image of the
-//     fp32 logits (NaN -> lowest) finds the topk-th largest key in at most
-//     three histogram passes (11, 11, 10 bits) over the row, stopping early
-//     when the threshold bin is taken whole;
-//   * a final pass writes every key above the threshold and the first
-//     (lowest-position) keys equal to it, in ascending position order, using
-//     block-wide prefix sums so the result is deterministic.
-// The row (<= 512 KB) is re-read from L2/MALL by each pass.
+// Method (MI355X design): rows with n <= topk keep 0..n-1 and read no
+// logits. Longer rows run a radix select on the order-preserving uint32 image
+// of the fp32 logits (NaN -> lowest, -0 -> +0):
+//   * pass 1 spreads every row over many blocks: 16-bit histograms of the
+//     top 12 key bits per 16384-position chunk;
+//   * pass 2 is one 1024-thread block per row: it sums the chunk histograms,
+//     finds the bin holding the topk-th largest key, then reads the row once,
+//     marking keys above that bin in an LDS bitmap of positions and gathering
+//     the keys inside it; two 10-bit radix passes over those candidates give
+//     the exact threshold, ties on it keep the lowest positions, and a scan of
+//     the bitmap writes the result in ascending position order, so the output
+//     does not depend on scheduling.
+// Rows longer than the bitmap, or whose threshold bin overflows the LDS
+// candidate store, take a slower multi-pass select over the row in global
+// memory.
 #include "common.h"
 
 namespace {
@@ -189,17 +194,39 @@ __device__ void select_multipass(const float* row, int n, bool vec, int topk,
 constexpr int kChunk = 16384;       // positions per histogram block
 constexpr int kHistBins = 4096;     // first digit: key bits 31..20
 constexpr int kHistThreads = 256;
-constexpr int kMaxAbove = 2048;     // fast path: topk <= 2048
 constexpr int kCap = 12288;         // fast path: threshold-bin candidates in LDS
+constexpr int kMapBits = 262144;    // fast path: rows of at most this many positions
+constexpr int kMapWords = kMapBits / 32;
+constexpr int kTieBins = 512;       // position radix for exact ties: 2 x 9 bits
+constexpr int kBatch = 4;           // float4 per thread per batch of the row pass
+
+static_assert(kMapBits == kTieBins * kTieBins, "tie radix spans the bitmap");
+
+// Raw values of positions pos..pos+3 with no branch around the loads (a load
+// under a branch makes the compiler wait for every load in flight). VEC: one
+// 16-byte load at min(pos, vlast), where vlast is a multiple of 4 with
+// vlast + 4 <= n; otherwise four loads clamped to n - 1. Values of positions
+// past the caller's bound are stale and the caller masks them.
+template <bool VEC>
+__device__ __forceinline__ void load4(const float* row, int pos, int vlast,
+                                      int n, float* v) {
+  if constexpr (VEC) {
+    const float4 x = *reinterpret_cast<const float4*>(row + min(pos, vlast));
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = row[min(pos + e, n - 1)];
+  }
+}
 
 // Pass 1: per-(row, chunk) histogram of the top 12 key bits, over all CUs.
 // Each wave counts into its own LDS sub-histogram; the block writes 4096
 // 16-bit counts (a chunk holds at most 16384 positions).
+template <bool VEC>
 __global__ void __launch_bounds__(kHistThreads)
 topk_hist_kernel(const float* __restrict__ logits, int64_t logits_stride,
                  const int32_t* __restrict__ lengths, int topk,
-                 int max_seqlen_k, int chunks, uint16_t* __restrict__ ws,
-                 bool vec) {
+                 int max_seqlen_k, int chunks, uint16_t* __restrict__ ws) {
   __shared__ uint32_t sub[4][kHistBins];
   const int64_t t = blockIdx.x / chunks;
   const int c = blockIdx.x % chunks;
@@ -212,32 +239,35 @@ topk_hist_kernel(const float* __restrict__ logits, int64_t logits_stride,
   uint4* z = reinterpret_cast<uint4*>(&sub[0][0]);
   for (int i = threadIdx.x; i < 4 * kHistBins / 4; i += kHistThreads)
     z[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
   const float* row = logits + t * logits_stride;
   uint32_t* h = sub[wave];
-  // all 64 positions of a thread are loaded before any is counted; load k
-  // of the block covers 1024 consecutive positions
-  constexpr int kPer = kChunk / kHistThreads / 4;   // 16 float4 per thread
-  float4 v[kPer];
+  // [start, vend) is read 4 positions at a time; with VEC the 0..3 positions
+  // of [vend, end) are read one per thread afterwards
+  const int vend = VEC ? min(end, n & ~3) : end;
+  constexpr int kPer = kChunk / kHistThreads / 4;   // 16 loads per thread
+  float v[kPer][4];
+  if (vend > start) {
+    // every load of the thread is issued before any value is counted; load k
+    // of the block covers 1024 consecutive positions
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int pos = start + k * (kHistThreads * 4) + threadIdx.x * 4;
-    if (vec && pos + 4 <= end) {
-      v[k] = *reinterpret_cast<const float4*>(row + pos);
-    } else {
-      v[k].x = pos < end ? row[pos] : 0.0f;
-      v[k].y = pos + 1 < end ? row[pos + 1] : 0.0f;
-      v[k].z = pos + 2 < end ? row[pos + 2] : 0.0f;
-      v[k].w = pos + 3 < end ? row[pos + 3] : 0.0f;
+    for (int k = 0; k < kPer; ++k)
+      load4<VEC>(row, start + k * (kHistThreads * 4) + threadIdx.x * 4,
+                 vend - 4, n, v[k]);
+  }
+  __syncthreads();   // sub-histograms cleared
+  if (vend > start) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int pos = start + k * (kHistThreads * 4) + threadIdx.x * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (pos + e < vend) atomicAdd(&h[order_key(v[k][e]) >> 20], 1u);
     }
   }
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int pos = start + k * (kHistThreads * 4) + threadIdx.x * 4;
-    if (pos < end) atomicAdd(&h[order_key(v[k].x) >> 20], 1u);
-    if (pos + 1 < end) atomicAdd(&h[order_key(v[k].y) >> 20], 1u);
-    if (pos + 2 < end) atomicAdd(&h[order_key(v[k].z) >> 20], 1u);
-    if (pos + 3 < end) atomicAdd(&h[order_key(v[k].w) >> 20], 1u);
+  if (VEC) {
+    const int t0 = max(start, vend);
+    if ((int)threadIdx.x < end - t0)
+      atomicAdd(&h[order_key(row[t0 + threadIdx.x]) >> 20], 1u);
   }
   __syncthreads();
   uint32_t* dst = reinterpret_cast<uint32_t*>(ws + (t * chunks + c) * kHistBins);
@@ -249,12 +279,15 @@ topk_hist_kernel(const float* __restrict__ logits, int64_t logits_stride,
   }
 }
 
-// Pass 2: one block per row. Sums the row's chunk histograms, finds the
-// threshold bin, then in one ordered pass over the row collects the
-// positions above it (list A) and the (key, position) candidates inside it
-// (list B) in LDS; resolves the exact threshold among the candidates with two
-// more 10-bit radix passes in LDS; merges A with the chosen candidates in
-// position order and writes them (through the page table when given).
+// Pass 2: one block per row. Sums the row's chunk histograms and finds the
+// threshold bin; one pass over the row then marks every key above that bin in
+// an LDS bitmap of positions and gathers the keys inside it as candidates
+// (unordered); the exact threshold comes from two more 10-bit radix passes
+// over the candidates, and ties on the threshold key keep the lowest
+// positions (a radix select on position). The chosen candidates are marked
+// too, and a block-wide scan of the bitmap writes the kept positions in
+// ascending order (through the page table when given).
+template <bool VEC>
 __global__ void __launch_bounds__(kThreads)
 topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
                    const int32_t* __restrict__ lengths, int topk,
@@ -262,16 +295,17 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
                    const uint16_t* __restrict__ ws,
                    const int32_t* __restrict__ table, int64_t table_stride,
                    const int32_t* __restrict__ t2r, int32_t* __restrict__ out,
-                   int64_t out_stride, bool vec) {
+                   int64_t out_stride) {
   __shared__ uint32_t hist[kHistBins];
-  __shared__ int32_t list_a[kMaxAbove];
-  __shared__ int32_t sel_b[kMaxAbove];
+  __shared__ uint32_t bitmap[kMapWords];
   __shared__ uint32_t cand_key[kCap];
   __shared__ int32_t cand_pos[kCap];
   __shared__ int scan_buf[2 * kWaves + 1];
   __shared__ uint32_t s_sel[3];
+  __shared__ int s_ncand;
 
   const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
   int n = lengths[t];
   n = n < 0 ? 0 : (n > max_seqlen_k ? max_seqlen_k : n);
   int32_t* orow = out + t * out_stride;
@@ -280,151 +314,180 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
     return trow ? (trow[i >> 6] << 6) + (i & 63) : i;
   };
   if (n <= topk) {
-    for (int j = threadIdx.x; j < topk; j += kThreads) orow[j] = j < n ? map(j) : -1;
+    for (int j = tid; j < topk; j += kThreads) orow[j] = j < n ? map(j) : -1;
     return;
   }
   const float* row = logits + t * logits_stride;
 
-  // ---- row histogram of the top 12 key bits and its threshold bin
+  // ---- row histogram of the top 12 key bits and its threshold bin: each
+  // thread sums 4 bins of every chunk with 8-byte loads
   const int nch = (n + kChunk - 1) / kChunk;
   const uint16_t* hrow = ws + t * chunks * kHistBins;
-  for (int b = threadIdx.x; b < kHistBins; b += kThreads) {
-    uint32_t s = 0;
-    for (int c = 0; c < nch; ++c) s += hrow[c * kHistBins + b];
-    hist[b] = s;
+  {
+    static_assert(kThreads * 4 == kHistBins, "one thread per 4 bins");
+    const int b4 = tid * 4;
+    uint32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    for (int c = 0; c < nch; ++c) {
+      const uint2 v = *reinterpret_cast<const uint2*>(hrow + c * kHistBins + b4);
+      s0 += v.x & 0xFFFFu; s1 += v.x >> 16; s2 += v.y & 0xFFFFu; s3 += v.y >> 16;
+    }
+    *reinterpret_cast<uint4*>(&hist[b4]) = make_uint4(s0, s1, s2, s3);
   }
+  const int nw = (n + 31) >> 5;
+  if (n <= kMapBits)
+    for (int w = tid; w < nw; w += kThreads) bitmap[w] = 0u;
+  if (tid == 0) s_ncand = 0;
   __syncthreads();
   find_threshold_bin(hist, kHistBins, topk, s_sel);
   __syncthreads();
   const uint32_t bin = s_sel[0];
   int krem = (int)s_sel[1];
+  bool exact = s_sel[2] != 0;
   const uint32_t cnt_b = hist[bin];
   __syncthreads();
-  if (topk > kMaxAbove || cnt_b > (uint32_t)kCap) {
-    select_multipass(row, n, vec, topk, orow, map, hist, scan_buf, s_sel);
+  if (cnt_b > (uint32_t)kCap || n > kMapBits) {
+    select_multipass(row, n, VEC, topk, orow, map, hist, scan_buf, s_sel);
     return;
   }
 
-  // ---- one ordered pass: 32 consecutive positions per thread per round; the
-  // next round's loads are issued before this round's scan
-  constexpr int kRun = 32;
-  constexpr int kRound = kThreads * kRun;
-  auto load_round = [&](float4* v, int b0) {
-    const int base = b0 + threadIdx.x * kRun;
+  // ---- one pass over the row, batches of kBatch loads per thread, the next
+  // batch in flight while the current one is classified. Loads past the row
+  // are clamped onto its last vector, so the prefetch needs no branch.
+  const int lane = tid & 63;
+  const int vend = VEC ? (n & ~3) : n;
+  constexpr int kSpan = kThreads * 4;           // positions per load step
+  constexpr int kPerBatch = kSpan * kBatch;
+  float cur[kBatch][4];
+  if (vend > 0) {   // VEC rows of 1..3 positions are all tail
 #pragma unroll
-    for (int k = 0; k < kRun / 4; ++k) {
-      const int pos = base + 4 * k;
-      if (vec && pos + 4 <= n) {
-        v[k] = *reinterpret_cast<const float4*>(row + pos);
-      } else {
-        v[k].x = pos < n ? row[pos] : 0.0f;
-        v[k].y = pos + 1 < n ? row[pos + 1] : 0.0f;
-        v[k].z = pos + 2 < n ? row[pos + 2] : 0.0f;
-        v[k].w = pos + 3 < n ? row[pos + 3] : 0.0f;
+    for (int j = 0; j < kBatch; ++j) load4<VEC>(row, j * kSpan + tid * 4, vend - 4, n, cur[j]);
+  }
+  for (int b0 = 0; b0 < vend; b0 += kPerBatch) {
+    float nxt[kBatch][4];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      load4<VEC>(row, b0 + kPerBatch + j * kSpan + tid * 4, vend - 4, n, nxt[j]);
+    uint32_t kb[kBatch][4];
+    int ce = 0;   // candidates of this thread in the batch
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int pos = b0 + j * kSpan + tid * 4;
+      uint32_t m = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kb[j][e] = order_key(cur[j][e]);
+        const bool in = pos + e < vend;
+        const uint32_t d = kb[j][e] >> 20;
+        m |= (in && d > bin) ? (1u << e) : 0u;
+        ce += (in && d == bin) ? 1 : 0;
       }
+      if (m) atomicOr(&bitmap[pos >> 5], m << (pos & 31));
     }
-  };
-  int na = 0, nb = 0;
-  float4 cur[kRun / 4], nxt[kRun / 4];
-  load_round(cur, 0);
-  for (int base0 = 0; base0 < n; base0 += kRound) {
-    if (base0 + kRound < n) load_round(nxt, base0 + kRound);
-    const int base = base0 + threadIdx.x * kRun;
-    uint32_t kb[kRun];
+    // one LDS atomic per wave reserves the wave's candidate slots
+    int incl = ce;
 #pragma unroll
-    for (int k = 0; k < kRun / 4; ++k) {
-      kb[4 * k] = order_key(cur[k].x); kb[4 * k + 1] = order_key(cur[k].y);
-      kb[4 * k + 2] = order_key(cur[k].z); kb[4 * k + 3] = order_key(cur[k].w);
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
     }
-    int ga = 0, gb = 0;
+    int base = 0;
+    if (lane == 63 && incl > 0) base = atomicAdd(&s_ncand, incl);
+    base = __shfl(base, 63);
+    if (ce) {
+      int q = base + incl - ce;
 #pragma unroll
-    for (int k = 0; k < kRun; ++k) {
-      const uint32_t d = kb[k] >> 20;
-      const bool in = base + k < n;
-      ga += (in && d > bin);
-      gb += (in && d == bin);
-    }
-    int tot;
-    const int off = block_exclusive_scan(ga | (gb << 16), scan_buf, &tot);
-    int pa = na + (off & 0xFFFF), pb = nb + (off >> 16);
+      for (int j = 0; j < kBatch; ++j) {
+        const int pos = b0 + j * kSpan + tid * 4;
 #pragma unroll
-    for (int k = 0; k < kRun; ++k) {
-      const uint32_t d = kb[k] >> 20;
-      if (base + k < n) {
-        if (d > bin) {
-          if (pa < kMaxAbove) list_a[pa] = base + k;
-          ++pa;
-        } else if (d == bin) {
-          if (pb < kCap) { cand_key[pb] = kb[k]; cand_pos[pb] = base + k; }
-          ++pb;
+        for (int e = 0; e < 4; ++e) {
+          if (pos + e < vend && (kb[j][e] >> 20) == bin) {
+            if (q < kCap) { cand_key[q] = kb[j][e]; cand_pos[q] = pos + e; }
+            ++q;
+          }
         }
       }
     }
-    na += tot & 0xFFFF;
-    nb += tot >> 16;
 #pragma unroll
-    for (int k = 0; k < kRun / 4; ++k) cur[k] = nxt[k];
+    for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cur[j][e] = nxt[j][e];
+  }
+  if (VEC && tid < n - vend) {   // the 0..3 positions past the last vector
+    const int pos = vend + tid;
+    const uint32_t k = order_key(row[pos]);
+    if ((k >> 20) > bin) {
+      atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
+    } else if ((k >> 20) == bin) {
+      const int q = atomicAdd(&s_ncand, 1);
+      if (q < kCap) { cand_key[q] = k; cand_pos[q] = pos; }
+    }
   }
   __syncthreads();
-  na = min(na, kMaxAbove);
-  nb = min(nb, kCap);
+  const int nc = min(s_ncand, kCap);
 
   // ---- exact threshold among the candidates (bits 19..10, then 9..0)
   uint32_t prefix = bin << 20, pmask = 0xFFF00000u;
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 2 && !exact; ++pass) {
     const int shift = pass == 0 ? 10 : 0;
-    for (int b = threadIdx.x; b < 1024; b += kThreads) hist[b] = 0;
+    hist[tid] = 0;   // 1024 bins
     __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += kThreads) {
+    for (int i = tid; i < nc; i += kThreads) {
       const uint32_t k = cand_key[i];
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1u);
     }
     __syncthreads();
     find_threshold_bin(hist, 1024, krem, s_sel);
     __syncthreads();
-    const uint32_t b2 = s_sel[0];
-    krem = (int)s_sel[1];
-    const bool exact = s_sel[2] != 0;
-    prefix |= b2 << shift;
+    prefix |= s_sel[0] << shift;
     pmask |= 1023u << shift;
+    krem = (int)s_sel[1];
+    exact = s_sel[2] != 0;
     __syncthreads();
-    if (exact) break;
   }
-
-  // ---- chosen candidates, in position order
-  int eq_run = 0, nsel = 0;
-  for (int i0 = 0; i0 < nb; i0 += kThreads) {
-    const int i = i0 + threadIdx.x;
-    const uint32_t mk = i < nb ? (cand_key[i] & pmask) : 0u;
-    const int gt = i < nb && mk > prefix;
-    const int eq = i < nb && mk == prefix;
-    int eq_tot;
-    const int er = eq_run + block_exclusive_scan(eq, scan_buf, &eq_tot);
-    const int sel = gt || (eq && er < krem);
-    int sel_tot;
-    const int ps = nsel + block_exclusive_scan(sel, scan_buf, &sel_tot);
-    if (sel && ps < kMaxAbove) sel_b[ps] = cand_pos[i];
-    eq_run += eq_tot;
-    nsel += sel_tot;
+  // ---- equal full keys at the threshold: keep the krem lowest positions,
+  // a radix select on tk = kMapBits - 1 - position (unique, so exact)
+  uint32_t tprefix = 0, tmask = 0;
+  for (int pass = 0; pass < 2 && !exact; ++pass) {
+    const int shift = pass == 0 ? 9 : 0;
+    if (tid < kTieBins) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < nc; i += kThreads) {
+      const uint32_t tk = (uint32_t)(kMapBits - 1 - cand_pos[i]);
+      if (cand_key[i] == prefix && (tk & tmask) == tprefix)
+        atomicAdd(&hist[(tk >> shift) & (kTieBins - 1)], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin(hist, kTieBins, krem, s_sel);
+    __syncthreads();
+    tprefix |= s_sel[0] << shift;
+    tmask |= (uint32_t)(kTieBins - 1) << shift;
+    krem = (int)s_sel[1];
+    __syncthreads();
+  }
+  for (int i = tid; i < nc; i += kThreads) {
+    const uint32_t mk = cand_key[i] & pmask;
+    const int pos = cand_pos[i];
+    const bool keep = mk > prefix ||
+        (mk == prefix && (exact || (uint32_t)(kMapBits - 1 - pos) >= tprefix));
+    if (keep) atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
   }
   __syncthreads();
-  nsel = min(nsel, kMaxAbove);
 
-  // ---- merge the two position-sorted lists: rank = own index + number of
-  // smaller entries in the other list
-  for (int i = threadIdx.x; i < na; i += kThreads) {
-    const int v = list_a[i];
-    int lo = 0, hi = nsel;
-    while (lo < hi) { const int m = (lo + hi) >> 1; if (sel_b[m] < v) lo = m + 1; else hi = m; }
-    const int r = i + lo;
-    if (r < topk) orow[r] = map(v);
-  }
-  for (int j = threadIdx.x; j < nsel; j += kThreads) {
-    const int v = sel_b[j];
-    int lo = 0, hi = na;
-    while (lo < hi) { const int m = (lo + hi) >> 1; if (list_a[m] < v) lo = m + 1; else hi = m; }
-    const int r = j + lo;
-    if (r < topk) orow[r] = map(v);
+  // ---- kept positions in ascending order: each thread owns a run of words
+  const int per = (nw + kThreads - 1) / kThreads;
+  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
+  int tot;
+  int o = block_exclusive_scan(cnt, scan_buf, &tot);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = bitmap[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (o < topk) orow[o] = map(w * 32 + b);
+      ++o;
+    }
   }
 }
 
@@ -484,14 +547,16 @@ extern "C" int nsa_topk_transform(const float* logits, int64_t logits_stride,
   if (need > 0) {
     const int64_t hb = (int64_t)T * chunks;
     NSA_REQUIRE(hb < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
-    hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)hb), dim3(kHistThreads), 0,
-                       s, logits, logits_stride, lengths, topk, max_seqlen_k,
-                       chunks, ws, vec);
+    auto hist = vec ? topk_hist_kernel<true> : topk_hist_kernel<false>;
+    hipLaunchKernelGGL(hist, dim3((unsigned)hb), dim3(kHistThreads), 0, s,
+                       logits, logits_stride, lengths, topk, max_seqlen_k,
+                       chunks, ws);
     int st = nsa::check_launch(fn);
     if (st != NSA_OK) return st;
   }
-  hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kThreads), 0, s, logits,
-                     logits_stride, lengths, topk, max_seqlen_k, chunks, ws,
-                     table, table_stride, token_to_req, out, out_stride, vec);
+  auto sel = vec ? topk_select_kernel<true> : topk_select_kernel<false>;
+  hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, s, logits, logits_stride,
+                     lengths, topk, max_seqlen_k, chunks, ws, table,
+                     table_stride, token_to_req, out, out_stride);
   return nsa::check_launch(fn);
 }
