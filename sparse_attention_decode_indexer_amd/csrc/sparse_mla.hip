@@ -485,6 +485,364 @@ sparse_mla_kernel(const Params p) {
   }
 }
 
+// ---- 64 heads per block (H a multiple of 64) --------------------------------
+// One 512-thread block (8 waves) per (row, 64 heads, KV split), one block per
+// CU. Wave (ht = w % 4, dw = w / 4) owns heads 16*ht.. of the block and half
+// dw of the work: contraction dims of 128-blocks 2dw, 2dw+1 plus rope step
+// 16+dw for S, and value dims 256*dw.. for O. The two halves of a head
+// tile's scores meet in LDS and are added in the same order in both waves,
+// so both run an identical softmax. The split's slot ids and per-step valid
+// masks are loaded into LDS once; the bf16 K tile is double-buffered (two
+// barriers per step: score exchange and tile swap); the gather of step s+3
+// is issued while step s is computed, from two register stages that
+// alternate (the step loop is unrolled by two, so no register copy waits on
+// a load in flight).
+constexpr int kThreadsW = 512;
+constexpr int kMaxSplit = 2048;                // slots per block
+constexpr int kIdsCap = 5 * kThreadsW;         // 2560 >= kMaxSplit + 4 steps of overrun
+constexpr int kMaskCap = kIdsCap / kStep;      // 80 steps
+
+// Gather registers of one thread of a 512-thread block for one step: slot
+// qd = tid / 16 of the step, 16-byte chunks cc and cc + 16 of its value part
+// and 8 bytes of its rope part.
+template <bool FP8>
+struct StageW;
+
+template <>
+struct StageW<true> {   // 656-byte rows
+  uint2 code[4];         // codes 8cc + 128k .. +8 (block k)
+  float scale;           // block scale cc % 4 of the slot
+  uint2 rope;
+  bool valid;
+  __device__ __forceinline__ void load(const Params& p, const int32_t* ids, int tid) {
+    const int qd = tid >> 4, cc = tid & 15;
+    const int32_t slot = ids[qd];
+    valid = slot >= 0;
+    const uint8_t* row = p.kv + (int64_t)(slot >= 0 ? slot : 0) * 656;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) code[k] = *reinterpret_cast<const uint2*>(row + 8 * cc + 128 * k);
+    scale = *reinterpret_cast<const float*>(row + 512 + 4 * (cc & 3));
+    rope = *reinterpret_cast<const uint2*>(row + 528 + 8 * cc);
+  }
+  // exact fp8 -> bf16 (every e4m3 value is a bf16 value: the upper halves of
+  // the fp32 images); the block scales go to LDS and are applied to the
+  // scores and to P. Consecutive lanes write consecutive 16-byte pieces.
+  __device__ __forceinline__ void store(uint8_t* kt, float* scl, int tid) const {
+    const int qd = tid >> 4, cc = tid & 15;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint2 cs = valid ? code[k] : make_uint2(0, 0);
+      uint32_t bf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t wi = i == 0 ? cs.x : cs.y;
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wi, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wi, true);
+        bf[2 * i] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+        bf[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+      }
+      *reinterpret_cast<uint4*>(kt + qd * kKsRow + 16 * cc + 256 * k) =
+          make_uint4(bf[0], bf[1], bf[2], bf[3]);
+    }
+    // 4 lanes of the slot write each block scale (identical values)
+    scl[qd * 4 + (cc & 3)] = valid ? scale : 0.0f;
+    *reinterpret_cast<uint2*>(kt + qd * kKsRow + kDV * 2 + 8 * cc) =
+        valid ? rope : make_uint2(0, 0);
+  }
+};
+
+template <>
+struct StageW<false> {  // 576 bf16 rows
+  uint4 v[4];
+  uint2 rope;
+  bool valid;
+  __device__ __forceinline__ void load(const Params& p, const int32_t* ids, int tid) {
+    const int qd = tid >> 4, cc = tid & 15;
+    const int32_t slot = ids[qd];
+    valid = slot >= 0;
+    const uint8_t* row = p.kv + (int64_t)(slot >= 0 ? slot : 0) * (kDQK * 2);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) v[h] = *reinterpret_cast<const uint4*>(row + 16 * (cc + 16 * h));
+    rope = *reinterpret_cast<const uint2*>(row + kDV * 2 + 8 * cc);
+  }
+  __device__ __forceinline__ void store(uint8_t* kt, float*, int tid) const {
+    const int qd = tid >> 4, cc = tid & 15;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      *reinterpret_cast<uint4*>(kt + qd * kKsRow + 16 * (cc + 16 * h)) =
+          valid ? v[h] : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint2*>(kt + qd * kKsRow + kDV * 2 + 8 * cc) =
+        valid ? rope : make_uint2(0, 0);
+  }
+};
+
+template <bool FP8>
+__global__ void __launch_bounds__(kThreadsW, 1)
+sparse_mla_h64_kernel(const Params p) {
+  constexpr int NT = kDV / 2 / 16;           // 16 value-dim tiles per wave
+  constexpr int KS = kKSteps / 2;            // 9 contraction steps per wave
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2][kKsBytes];
+  __shared__ __attribute__((aligned(16))) float scl[2][FP8 ? kStep * 4 : 4];
+  __shared__ int32_t ids[kIdsCap];
+  __shared__ uint32_t vmask[kMaskCap];
+  __shared__ float xch[8][8][64];            // partial scores per wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int ht = wave & 3, dw = wave >> 2;
+
+  const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int hb = lb % p.n_hb;
+  const int split = (lb / p.n_hb) % p.n_splits;
+  const int64_t t = lb / (p.n_hb * p.n_splits);
+  const int h0 = hb * 64 + ht * 16;          // first head of this wave
+
+  int n_row = p.num_slots > 0 ? p.topk : 0;
+  if (p.seqlens) {
+    const int sl = p.seqlens[t];
+    n_row = sl < 0 ? 0 : (sl < n_row ? sl : n_row);
+  }
+  const int s_begin = split * p.split_slots;
+  const int n = min(s_begin + p.split_slots, n_row) - s_begin;   // may be <= 0
+  const int nsteps = n > 0 ? (n + kStep - 1) / kStep : 0;
+
+  // ---- slot ids of the split (validated; -1 past its end) and step masks
+  {
+    const int32_t* irow = p.idx + t * p.idx_stride + s_begin;
+    const int last = n > 0 ? n - 1 : 0;
+    int32_t v[kIdsCap / kThreadsW];
+#pragma unroll
+    for (int k = 0; k < kIdsCap / kThreadsW; ++k) v[k] = irow[min(tid + k * kThreadsW, last)];
+#pragma unroll
+    for (int k = 0; k < kIdsCap / kThreadsW; ++k) {
+      const int i = tid + k * kThreadsW;
+      const int32_t id = v[k];
+      ids[i] = (i < n && id >= 0 && id < p.num_slots) ? id : -1;
+    }
+  }
+  __syncthreads();
+  for (int k = wave; k < kMaskCap; k += 8) {
+    const bool ok = lane < kStep && ids[k * kStep + (lane & (kStep - 1))] >= 0;
+    const unsigned long long b = __ballot(ok);
+    if (lane == 0) vmask[k] = (uint32_t)b;
+  }
+
+  // Q as the B operand of S^T = K.Q^T: lane (head c, group g) holds dims
+  // kstep*32 + 8g .. +8 of the wave's 9 contraction steps (blocks 2dw, 2dw+1
+  // and rope step 16 + dw)
+  bf16x8 qb[KS];
+  {
+    const uint16_t* qh = p.q + t * p.q_tok_stride + (int64_t)(h0 + c) * p.q_head_stride;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int kstep = i < 8 ? dw * 8 + i : 16 + dw;
+      qb[i] = *reinterpret_cast<const bf16x8*>(qh + kstep * 32 + g * 8);
+    }
+  }
+
+  f32x4 o[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;   // reference max (log2 domain) and sum of head c
+
+  // one step over the staged tile `kt` (block scales `sc` for an fp8 cache)
+  auto compute = [&](const uint8_t* kt, const float* sc, uint32_t valid) {
+    auto kfrag = [&](int mt, int kstep) {
+      return *reinterpret_cast<const bf16x8*>(kt + (mt * 16 + c) * kKsRow + (kstep * 32 + g * 8) * 2);
+    };
+    // ---- partial S^T over this wave's steps: two 128-dim blocks (fp8: each
+    // its own accumulator, scaled by the slot's block scale) and one rope
+    // step. The fragments of step kk+1 are read while step kk is multiplied;
+    // consecutive MFMAs go to independent accumulators.
+    f32x4 tb[3][2];
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) tb[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fr[2][2][2];   // [buffer][u][mt]
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) fr[0][u][mt] = kfrag(mt, dw * 8 + u * 4);
+#pragma unroll
+    for (int kk = 0; kk < 5; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk < 3) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) fr[nxt][u][mt] = kfrag(mt, dw * 8 + u * 4 + kk + 1);
+      } else if (kk == 3) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) fr[nxt][0][mt] = kfrag(mt, 16 + dw);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 4) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            tb[u][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[cur][u][mt], qb[u * 4 + kk], tb[u][mt], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          tb[2][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[cur][0][mt], qb[8], tb[2][mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane (head c, group g) holds slots mt*16 + 4g + r
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float part;
+        if constexpr (FP8) {
+          const float2 s2 = *reinterpret_cast<const float2*>(sc + (mt * 16 + 4 * g + r) * 4 + 2 * dw);
+          part = fmaf(s2.x, tb[0][mt][r], fmaf(s2.y, tb[1][mt][r], tb[2][mt][r]));
+        } else {
+          part = (tb[0][mt][r] + tb[1][mt][r]) + tb[2][mt][r];
+        }
+        xch[wave][mt * 4 + r][lane] = part;
+      }
+    __syncthreads();
+    // full scores: own half + partner half (a + b == b + a, so both waves of
+    // the pair hold identical scores); absent slots get -inf by adding it
+    float pv[2][4];
+    float lmx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sfull = xch[wave][mt * 4 + r][lane] + xch[wave ^ 4][mt * 4 + r][lane];
+        const int j = mt * 16 + 4 * g + r;
+        const float off = ((valid >> j) & 1u) ? 0.0f : -INFINITY;
+        pv[mt][r] = fmaf(sfull, p.scale_log2, off);
+        lmx = fmaxf(lmx, pv[mt][r]);
+      }
+
+    // ---- online softmax with a lazily raised reference max: O is rescaled
+    // only in the rare step where a score of a head exceeds its reference
+    // max by more than kLazy; l is kept per lane and summed at the end
+    if (__builtin_amdgcn_ballot_w64(lmx > m + kLazy) != 0) {
+      float mx = lmx;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool upd = mx > m + kLazy;        // same in the head's 4 lanes
+      const float alpha = upd ? exp2f(m - mx) : 1.0f;   // m = -inf -> 0
+      if (upd) m = mx;
+      l *= alpha;
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
+    }
+    // exponents are at most kLazy; weights below 2^-126 may flush to zero
+    const float m_use = m == -INFINITY ? 0.0f : m;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[mt][r] = __builtin_amdgcn_exp2f(pv[mt][r] - m_use);
+        l += pv[mt][r];
+      }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- P . V over this wave's two value blocks; for an fp8 cache P
+    // carries the slot's scale of the block. The B fragments of tile j+1 are
+    // read while tile j is multiplied.
+    auto vfrag = [&](int vb, int j) {
+      const uint8_t* src = kt + (4 * g + (c >> 2)) * kKsRow + (vb * 128 + j * 16 + 4 * (c & 3)) * 2;
+      const v4i16 b0 = read_tr(src);
+      const v4i16 b1 = read_tr(src + 16 * kKsRow);
+      const v4i16 bb[2] = {b0, b1};
+      return *reinterpret_cast<const bf16x8*>(bb);
+    };
+    bf16x8 vf[2];
+    vf[0] = vfrag(dw * 2, 0);
+#pragma unroll
+    for (int vh = 0; vh < 2; ++vh) {
+      const int vb = dw * 2 + vh;
+      bf16x8 pa;
+      {
+        float q8[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float s = 1.0f;
+            if constexpr (FP8) s = sc[(mt * 16 + 4 * g + r) * 4 + vb];
+            q8[mt][r] = pv[mt][r] * s;
+          }
+        const uint4 u = make_uint4(pack_bf16x2_hw(q8[0][0], q8[0][1]), pack_bf16x2_hw(q8[0][2], q8[0][3]),
+                                   pack_bf16x2_hw(q8[1][0], q8[1][1]), pack_bf16x2_hw(q8[1][2], q8[1][3]));
+        pa = *reinterpret_cast<const bf16x8*>(&u);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = vh * 8 + j;             // tile index within the wave
+        if (q + 1 < NT) vf[(q + 1) & 1] = vfrag(dw * 2 + (q + 1) / 8, (q + 1) % 8);
+        __builtin_amdgcn_sched_barrier(0);
+        o[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vf[q & 1], o[q], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    StageW<FP8> sa, sb;
+    sa.load(p, ids, tid);
+    sb.load(p, ids + kStep, tid);
+    sa.store(ks[0], scl[0], tid);
+    sa.load(p, ids + 2 * kStep, tid);
+    __syncthreads();
+    for (int s = 0; s < nsteps; s += 2) {
+      sb.store(ks[1], scl[1], tid);                 // step s + 1
+      sb.load(p, ids + (s + 3) * kStep, tid);       // step s + 3
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ks[0], scl[0], vmask[s]);
+      __syncthreads();
+      sa.store(ks[0], scl[0], tid);                 // step s + 2
+      sa.load(p, ids + (s + 4) * kStep, tid);       // step s + 4
+      __builtin_amdgcn_sched_barrier(0);
+      compute(ks[1], scl[1], vmask[s + 1]);         // empty when s + 1 == nsteps
+      __syncthreads();
+    }
+  }
+
+  // ---- finalize: lane (dim c of tile nt, group g) holds O[head 4g+r][dim]
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float lr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lr[r] = __shfl(l, 4 * g + r);
+  const float lse_val = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  const int d0 = dw * (kDV / 2);
+  if (p.n_splits == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = lr[r] > 0.0f ? o[nt][r] / lr[r] : 0.0f;
+        p.out[(t * p.H + h0 + 4 * g + r) * kDV + d0 + nt * 16 + c] = (uint16_t)f32_to_bf16_bits(v);
+      }
+    if (p.lse && dw == 0 && g == 0) p.lse[t * p.H + h0 + c] = lse_val;
+  } else {
+    const int64_t base = ((int64_t)split * p.T + t) * p.H;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = lr[r] > 0.0f ? o[nt][r] / lr[r] : 0.0f;
+        p.ws_o[(base + h0 + 4 * g + r) * kDV + d0 + nt * 16 + c] = v;
+      }
+    if (dw == 0 && g == 0) p.ws_lse[base + h0 + c] = lse_val;
+  }
+}
+
 // Merge of KV-split partials, in split order: one wave per (row, head).
 __global__ void __launch_bounds__(256)
 combine_splits_kernel(const float* __restrict__ ws_o,
@@ -522,21 +880,29 @@ combine_splits_kernel(const float* __restrict__ ws_o,
 }
 
 struct Plan {
+  bool wide;   // 64 heads per block (sparse_mla_h64_kernel)
   int nh, hw, hb_heads, n_hb, n_splits, split_slots;
 };
 
+// Heads per block and KV splits: the 64-head kernel runs one block per CU,
+// so it aims at 256 blocks (one per CU) and at most kMaxSplit slots per
+// block; the narrower kernel runs two blocks per CU.
 Plan make_plan(int T, int H, int topk, bool decode) {
   Plan pl;
-  if (H % 32 == 0) { pl.nh = 1; pl.hw = 2; }
+  pl.wide = H % 64 == 0;
+  if (pl.wide) { pl.nh = 1; pl.hw = 4; }
+  else if (H % 32 == 0) { pl.nh = 1; pl.hw = 2; }
   else { pl.nh = 1; pl.hw = 1; }
   pl.hb_heads = 16 * pl.nh * pl.hw;
   pl.n_hb = H / pl.hb_heads;
   const int64_t base = (int64_t)T * pl.n_hb;
   const int max_splits = (topk + 127) / 128;   // >= 128 slots per split
+  const int min_splits = pl.wide ? (topk + kMaxSplit - 1) / kMaxSplit : 1;
   int ns = 1;
-  const int64_t target = decode ? 256 : 128;
+  const int64_t target = (pl.wide || decode) ? 256 : 128;
   if (base < target) ns = (int)((target + base - 1) / base);
   ns = ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
+  ns = ns < min_splits ? min_splits : ns;
   int ss = (topk + ns - 1) / ns;
   ss = (ss + kStep - 1) / kStep * kStep;
   ns = (topk + ss - 1) / ss;
@@ -618,14 +984,20 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
   NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: grid too large", fn);
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = kv_dtype == NSA_KV_FP8_656;
-  const dim3 grid((unsigned)blocks), block(kThreads);
+  const dim3 grid((unsigned)blocks), block(pl.wide ? kThreadsW : kThreads);
 #define NSA_MLA_LAUNCH(NH, HW)                                                      \
   do {                                                                            \
     if (fp8) hipLaunchKernelGGL((sparse_mla_kernel<NH, HW, true>), grid, block, 0, s, p); \
     else hipLaunchKernelGGL((sparse_mla_kernel<NH, HW, false>), grid, block, 0, s, p);    \
   } while (0)
-  if (pl.hw == 2) NSA_MLA_LAUNCH(1, 2);
-  else NSA_MLA_LAUNCH(1, 1);
+  if (pl.wide) {
+    if (fp8) hipLaunchKernelGGL(sparse_mla_h64_kernel<true>, grid, block, 0, s, p);
+    else hipLaunchKernelGGL(sparse_mla_h64_kernel<false>, grid, block, 0, s, p);
+  } else if (pl.hw == 2) {
+    NSA_MLA_LAUNCH(1, 2);
+  } else {
+    NSA_MLA_LAUNCH(1, 1);
+  }
 #undef NSA_MLA_LAUNCH
   st = nsa::check_launch(fn);
   if (st != NSA_OK || pl.n_splits == 1) return st;

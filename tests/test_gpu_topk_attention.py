@@ -98,7 +98,10 @@ def _random_case(rng, T, H, topk, num_slots, kind, frac_pad=0.1):
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
 @pytest.mark.parametrize("T,H,topk", [(1, 16, 2048), (3, 128, 2048), (5, 64, 256),
-                                      (2, 32, 100), (40, 16, 64), (4, 48, 512)])
+                                      (2, 32, 100), (40, 16, 64), (4, 48, 512),
+                                      # 64-head blocks: many splits, an odd last
+                                      # step of a split, > 2048 slots per row
+                                      (2, 128, 300), (200, 64, 96), (1, 64, 4096)])
 def test_sparse_mla_decode(kind, T, H, topk):
     nsa = need_gpu()
     note(f"sparse_mla {kind} T={T} H={H} topk={topk}")
