@@ -7,7 +7,12 @@
 //   s_i = sm_scale * q[t,h,:576] . K_i[:576],  o = softmax(s) . K[:, :512],
 //   lse = log sum_i exp(s_i).
 //
-// MI355X design (one 256-thread block = 4 waves):
+// Two kernels. An fp8 cache with H a multiple of 64 (the decode shape of the
+// large models) runs the 64-head kernel further below: 32x32 MFMA tiles, a
+// K tile dequantized once per step for 64 heads, software-pipelined steps.
+// Other shapes (16..48 heads, bf16 caches) run the narrower kernel:
+//
+// MI355X design of the narrower kernel (one 256-thread block = 4 waves):
 //   * a block owns one query row, HB = 16*NH*HW heads and one KV split; wave
 //     w owns NH head tiles of 16 (tile w % HW) and dim slice w / HW of
 //     DW = 4 / HW slices (16-head models use all 4 waves by splitting the 576
@@ -485,118 +490,128 @@ sparse_mla_kernel(const Params p) {
   }
 }
 
-// ---- 64 heads per block (H a multiple of 64) --------------------------------
-// One 512-thread block (8 waves) per (row, 64 heads, KV split), one block per
-// CU. Wave (ht = w % 4, dw = w / 4) owns heads 16*ht.. of the block and half
-// dw of the work: contraction dims of 128-blocks 2dw, 2dw+1 plus rope step
-// 16+dw for S, and value dims 256*dw.. for O. The two halves of a head
-// tile's scores meet in LDS and are added in the same order in both waves,
-// so both run an identical softmax. The split's slot ids and per-step valid
-// masks are loaded into LDS once; the bf16 K tile is double-buffered (two
-// barriers per step: score exchange and tile swap); the gather of step s+3
-// is issued while step s is computed, from two register stages that
-// alternate (the step loop is unrolled by two, so no register copy waits on
-// a load in flight).
-constexpr int kThreadsW = 512;
+// ---- 64 heads per block (H a multiple of 64, fp8 cache) --------------------
+// On gfx950 v_mfma_f32_32x32x16_bf16 runs at twice the rate of
+// v_mfma_f32_16x16x32_bf16 (measured), and a 32x32 tile also halves the LDS
+// fragment reads per flop, so this kernel works in 32x32 tiles.
+// One 256-thread block (4 waves, one per SIMD) per (row, 64 heads, KV
+// split), one block per CU. Wave (hg = w % 2, dw = w / 2) owns heads
+// 32*hg.. of the block and half dw of the work: S over contraction dims
+// 256dw..+256 and rope dims 512+32dw..+32 (18 steps of 16), O over value dims
+// 256dw..+256. The two halves of a head group's scores meet in LDS and are
+// added in the same order in both waves, so both run an identical softmax.
+// The gathered fp8 rows are dequantized to bf16 once per step (code times
+// block scale, rounded to nearest even) into a K tile that all four waves
+// read. The split's slot ids are loaded into LDS once; absent slots get a
+// -inf score bias written with the tile.
+// The steps are software-pipelined with one barrier per step: iteration k
+// stages the gathered rows of step k+1, computes the partial scores of step
+// k and runs softmax and P.V of step k-1 (three K tiles, two score-exchange
+// buffers). The gather of step k+3 is issued in iteration k from two
+// register stages that alternate (the loop is unrolled by two, so no
+// register copy waits on a load in flight).
+constexpr int kThreadsW = 256;
 constexpr int kMaxSplit = 2048;                // slots per block
-constexpr int kIdsCap = 5 * kThreadsW;         // 2560 >= kMaxSplit + 4 steps of overrun
-constexpr int kMaskCap = kIdsCap / kStep;      // 80 steps
+constexpr int kIdsCap = 10 * kThreadsW;        // 2560 >= kMaxSplit + 5 steps of overrun
 
-// Gather registers of one thread of a 512-thread block for one step: slot
-// qd = tid / 16 of the step, 16-byte chunks cc and cc + 16 of its value part
-// and 8 bytes of its rope part.
-template <bool FP8>
-struct StageW;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <>
-struct StageW<true> {   // 656-byte rows
-  uint2 code[4];         // codes 8cc + 128k .. +8 (block k)
-  float scale;           // block scale cc % 4 of the slot
-  uint2 rope;
+// Gather registers of one thread for one step: slot qd = tid / 8, 16-byte
+// code chunks cc + 8k (k = 0..3, chunk k lies in 128-block k), the slot's 4
+// block scales and 16 bytes of its rope part.
+struct StageF8 {
+  uint4 code[4];
+  float4 scale;
+  uint4 rope;
   bool valid;
   __device__ __forceinline__ void load(const Params& p, const int32_t* ids, int tid) {
-    const int qd = tid >> 4, cc = tid & 15;
+    const int qd = tid >> 3, cc = tid & 7;
     const int32_t slot = ids[qd];
     valid = slot >= 0;
     const uint8_t* row = p.kv + (int64_t)(slot >= 0 ? slot : 0) * 656;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) code[k] = *reinterpret_cast<const uint2*>(row + 8 * cc + 128 * k);
-    scale = *reinterpret_cast<const float*>(row + 512 + 4 * (cc & 3));
-    rope = *reinterpret_cast<const uint2*>(row + 528 + 8 * cc);
+    for (int k = 0; k < 4; ++k) code[k] = *reinterpret_cast<const uint4*>(row + 16 * (cc + 8 * k));
+    scale = *reinterpret_cast<const float4*>(row + 512);
+    rope = *reinterpret_cast<const uint4*>(row + 528 + 16 * cc);
   }
-  // exact fp8 -> bf16 (every e4m3 value is a bf16 value: the upper halves of
-  // the fp32 images); the block scales go to LDS and are applied to the
-  // scores and to P. Consecutive lanes write consecutive 16-byte pieces.
-  __device__ __forceinline__ void store(uint8_t* kt, float* scl, int tid) const {
-    const int qd = tid >> 4, cc = tid & 15;
+  // Staging in five parts (so it can be spread between MFMAs): part k < 4
+  // writes bf16(code * scale) of 128-block k, part 4 the rope dims and the
+  // score bias. An absent slot stores zeros (scale 0) and a -inf bias.
+  __device__ __forceinline__ void store_part(uint8_t* kt, float* bias, int tid, int part) const {
+    const int qd = tid >> 3, cc = tid & 7;
+    if (part < 4) {
+      const float sk = part == 0 ? scale.x : part == 1 ? scale.y : part == 2 ? scale.z : scale.w;
+      const float s = valid ? sk : 0.0f;
+      const uint32_t w[4] = {code[part].x, code[part].y, code[part].z, code[part].w};
+      uint32_t bf[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint2 cs = valid ? code[k] : make_uint2(0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+        bf[2 * i] = pack_bf16x2_hw(lo[0] * s, lo[1] * s);
+        bf[2 * i + 1] = pack_bf16x2_hw(hi[0] * s, hi[1] * s);
+      }
+      uint8_t* dst = kt + qd * kKsRow + 32 * (cc + 8 * part);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(bf[0], bf[1], bf[2], bf[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(bf[4], bf[5], bf[6], bf[7]);
+    } else {
+      const uint32_t msk = valid ? 0xFFFFFFFFu : 0u;
+      *reinterpret_cast<uint4*>(kt + qd * kKsRow + kDV * 2 + 16 * cc) =
+          make_uint4(rope.x & msk, rope.y & msk, rope.z & msk, rope.w & msk);
+      bias[qd] = valid ? 0.0f : -INFINITY;   // the slot's 8 lanes write the same value
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* kt, float* bias, int tid) const {
+#pragma unroll
+    for (int part = 0; part < 5; ++part) store_part(kt, bias, tid, part);
+  }
+  // Finer staging pieces: piece h < 8 writes 8 codes (half of 128-block
+  // h / 2) as 16 bytes of bf16, piece 8 the rope dims and the score bias.
+  __device__ __forceinline__ void store_piece(uint8_t* kt, float* bias, int tid, int h) const {
+    const int qd = tid >> 3, cc = tid & 7;
+    if (h < 8) {
+      const int part = h >> 1, half = h & 1;
+      const float sk = part == 0 ? scale.x : part == 1 ? scale.y : part == 2 ? scale.z : scale.w;
+      const float s = valid ? sk : 0.0f;
+      const uint32_t w0 = half == 0 ? code[part].x : code[part].z;
+      const uint32_t w1 = half == 0 ? code[part].y : code[part].w;
       uint32_t bf[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const uint32_t wi = i == 0 ? cs.x : cs.y;
+        const uint32_t wi = i == 0 ? w0 : w1;
         const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wi, false);
         const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wi, true);
-        bf[2 * i] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
-        bf[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+        bf[2 * i] = pack_bf16x2_hw(lo[0] * s, lo[1] * s);
+        bf[2 * i + 1] = pack_bf16x2_hw(hi[0] * s, hi[1] * s);
       }
-      *reinterpret_cast<uint4*>(kt + qd * kKsRow + 16 * cc + 256 * k) =
+      *reinterpret_cast<uint4*>(kt + qd * kKsRow + 32 * (cc + 8 * part) + 16 * half) =
           make_uint4(bf[0], bf[1], bf[2], bf[3]);
+    } else {
+      store_part(kt, bias, tid, 4);
     }
-    // 4 lanes of the slot write each block scale (identical values)
-    scl[qd * 4 + (cc & 3)] = valid ? scale : 0.0f;
-    *reinterpret_cast<uint2*>(kt + qd * kKsRow + kDV * 2 + 8 * cc) =
-        valid ? rope : make_uint2(0, 0);
   }
 };
 
-template <>
-struct StageW<false> {  // 576 bf16 rows
-  uint4 v[4];
-  uint2 rope;
-  bool valid;
-  __device__ __forceinline__ void load(const Params& p, const int32_t* ids, int tid) {
-    const int qd = tid >> 4, cc = tid & 15;
-    const int32_t slot = ids[qd];
-    valid = slot >= 0;
-    const uint8_t* row = p.kv + (int64_t)(slot >= 0 ? slot : 0) * (kDQK * 2);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) v[h] = *reinterpret_cast<const uint4*>(row + 16 * (cc + 16 * h));
-    rope = *reinterpret_cast<const uint2*>(row + kDV * 2 + 8 * cc);
-  }
-  __device__ __forceinline__ void store(uint8_t* kt, float*, int tid) const {
-    const int qd = tid >> 4, cc = tid & 15;
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      *reinterpret_cast<uint4*>(kt + qd * kKsRow + 16 * (cc + 16 * h)) =
-          valid ? v[h] : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint2*>(kt + qd * kKsRow + kDV * 2 + 8 * cc) =
-        valid ? rope : make_uint2(0, 0);
-  }
-};
-
-template <bool FP8>
 __global__ void __launch_bounds__(kThreadsW, 1)
 sparse_mla_h64_kernel(const Params p) {
-  constexpr int NT = kDV / 2 / 16;           // 16 value-dim tiles per wave
-  constexpr int KS = kKSteps / 2;            // 9 contraction steps per wave
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2][kKsBytes];
-  __shared__ __attribute__((aligned(16))) float scl[2][FP8 ? kStep * 4 : 4];
+  constexpr int KS = 18;                     // contraction steps of 16 per wave
+  constexpr int ND = 8;                      // value tiles of 32 dims per wave
+  __shared__ __attribute__((aligned(16))) uint8_t ks[3][kKsBytes];
+  __shared__ __attribute__((aligned(16))) float bias[3][kStep];
   __shared__ int32_t ids[kIdsCap];
-  __shared__ uint32_t vmask[kMaskCap];
-  __shared__ float xch[8][8][64];            // partial scores per wave
+  __shared__ __attribute__((aligned(16))) float xch[2][4][4][64][4];   // partial S per wave
+  __shared__ int s_ovf;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const int ht = wave & 3, dw = wave >> 2;
+  const int c32 = lane & 31, kg = lane >> 5;
+  const int hg = wave & 1, dw = wave >> 1;
 
   const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int hb = lb % p.n_hb;
   const int split = (lb / p.n_hb) % p.n_splits;
   const int64_t t = lb / (p.n_hb * p.n_splits);
-  const int h0 = hb * 64 + ht * 16;          // first head of this wave
+  const int h0 = hb * 64 + hg * 32;          // first head of this wave
 
   int n_row = p.num_slots > 0 ? p.topk : 0;
   if (p.seqlens) {
@@ -607,7 +622,7 @@ sparse_mla_h64_kernel(const Params p) {
   const int n = min(s_begin + p.split_slots, n_row) - s_begin;   // may be <= 0
   const int nsteps = n > 0 ? (n + kStep - 1) / kStep : 0;
 
-  // ---- slot ids of the split (validated; -1 past its end) and step masks
+  // ---- slot ids of the split (validated; -1 past its end)
   {
     const int32_t* irow = p.idx + t * p.idx_stride + s_begin;
     const int last = n > 0 ? n - 1 : 0;
@@ -621,225 +636,244 @@ sparse_mla_h64_kernel(const Params p) {
       ids[i] = (i < n && id >= 0 && id < p.num_slots) ? id : -1;
     }
   }
-  __syncthreads();
-  for (int k = wave; k < kMaskCap; k += 8) {
-    const bool ok = lane < kStep && ids[k * kStep + (lane & (kStep - 1))] >= 0;
-    const unsigned long long b = __ballot(ok);
-    if (lane == 0) vmask[k] = (uint32_t)b;
-  }
 
-  // Q as the B operand of S^T = K.Q^T: lane (head c, group g) holds dims
-  // kstep*32 + 8g .. +8 of the wave's 9 contraction steps (blocks 2dw, 2dw+1
-  // and rope step 16 + dw)
+  // Q as the B operand of S^T = K.Q^T: lane (head c32, group kg) holds dims
+  // 16*kstep + 8kg .. +8 of the wave's 18 steps
+  auto kstep_of = [&](int i) { return i < 16 ? dw * 16 + i : 32 + 2 * dw + (i - 16); };
   bf16x8 qb[KS];
   {
-    const uint16_t* qh = p.q + t * p.q_tok_stride + (int64_t)(h0 + c) * p.q_head_stride;
+    const uint16_t* qh = p.q + t * p.q_tok_stride + (int64_t)(h0 + c32) * p.q_head_stride;
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
-      const int kstep = i < 8 ? dw * 8 + i : 16 + dw;
-      qb[i] = *reinterpret_cast<const bf16x8*>(qh + kstep * 32 + g * 8);
+      qb[i] = *reinterpret_cast<const bf16x8*>(qh + kstep_of(i) * 16 + kg * 8);
+      asm volatile("" : "+a"(qb[i]));   // Q lives in AGPRs (MFMA reads it there)
     }
   }
 
-  f32x4 o[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.0f;   // reference max (log2 domain) and sum of head c
+  f32x16 o[ND];
+  // Softmax without rescaling O: the reference max m of a head is fixed at
+  // the first step with a valid slot (O and l are zero until then), and
+  // exponents are clamped at kMaxExp, which fp32 O and l absorb (|O| stays
+  // far below the fp32 range). A score beyond m + kMaxExp sets `ovf` and the
+  // split is run again with m = the true maximum mall (no score exceeds it).
+  constexpr float kMaxExp = 64.0f;
+  float m, l, mall;
+  bool ovf;
 
-  // one step over the staged tile `kt` (block scales `sc` for an fp8 cache)
-  auto compute = [&](const uint8_t* kt, const float* sc, uint32_t valid) {
-    auto kfrag = [&](int mt, int kstep) {
-      return *reinterpret_cast<const bf16x8*>(kt + (mt * 16 + c) * kKsRow + (kstep * 32 + g * 8) * 2);
+  // ---- one pipelined iteration k as explicit instruction groups (separated
+  // by scheduling barriers). Group g holds: the MFMA of contraction step g of
+  // the partial S^T(k) (g < 18; one accumulator chain, consecutive chain
+  // MFMAs separated by other work), the MFMA q = g - 6 of O += P(k-1).V
+  // (6 <= g < 22; q = ch * ND + d, so consecutive ones update different value
+  // tiles), and a slice of VALU work: the softmax of step k-1 in groups 0..5
+  // (P is needed from group 6 on), the staging of step k+1 in groups 6..14,
+  // the exchange write of S^T(k) in groups 18..21 and the gather of step k+3
+  // in group 21. A wave issues in order and its VALU only partly overlaps its
+  // MFMAs, so the slices are kept short. Fragments are read kPf MFMAs ahead
+  // into rings of kPf + 2, and a fragment is kept live one MFMA longer, so a
+  // read never overwrites the operand of the MFMA just issued. Lane
+  // (head c32, kg) element e of S^T holds slot 8(e/4) + 4kg + e%4; O element
+  // e of value tile d holds head 8(e/4) + 4kg + e%4 at dim d*32 + c32 of the
+  // wave's half.
+  constexpr int kPf = 2;                     // fragment prefetch distance
+  constexpr int kRing = kPf + 2;
+  constexpr int kPv0 = 6;                    // first group with a P.V MFMA
+  constexpr int kGroups = kPv0 + 2 * ND;     // 22
+  const int grp = lane >> 4, sl = lane & 15;
+  auto iter = [&](int k, StageF8& st, int xp, int xc) {
+    const uint8_t* ktc = ks[k % 3];          // step k: scores
+    const uint8_t* ktp = ks[(k + 2) % 3];    // step k-1: softmax and P.V
+    uint8_t* ktn = ks[(k + 1) % 3];          // step k+1: staged now
+    const float* bsp = bias[(k + 2) % 3];
+    float* bsn = bias[(k + 1) % 3];
+    auto kfrag = [&](int i) {
+      return *reinterpret_cast<const bf16x8*>(ktc + c32 * kKsRow + (kstep_of(i) * 16 + kg * 8) * 2);
     };
-    // ---- partial S^T over this wave's steps: two 128-dim blocks (fp8: each
-    // its own accumulator, scaled by the slot's block scale) and one rope
-    // step. The fragments of step kk+1 are read while step kk is multiplied;
-    // consecutive MFMAs go to independent accumulators.
-    f32x4 tb[3][2];
-#pragma unroll
-    for (int u = 0; u < 3; ++u)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) tb[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 fr[2][2][2];   // [buffer][u][mt]
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) fr[0][u][mt] = kfrag(mt, dw * 8 + u * 4);
-#pragma unroll
-    for (int kk = 0; kk < 5; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk < 3) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) fr[nxt][u][mt] = kfrag(mt, dw * 8 + u * 4 + kk + 1);
-      } else if (kk == 3) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) fr[nxt][0][mt] = kfrag(mt, 16 + dw);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk < 4) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-            tb[u][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[cur][u][mt], qb[u * 4 + kk], tb[u][mt], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          tb[2][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[cur][0][mt], qb[8], tb[2][mt], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // lane (head c, group g) holds slots mt*16 + 4g + r
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float part;
-        if constexpr (FP8) {
-          const float2 s2 = *reinterpret_cast<const float2*>(sc + (mt * 16 + 4 * g + r) * 4 + 2 * dw);
-          part = fmaf(s2.x, tb[0][mt][r], fmaf(s2.y, tb[1][mt][r], tb[2][mt][r]));
-        } else {
-          part = (tb[0][mt][r] + tb[1][mt][r]) + tb[2][mt][r];
-        }
-        xch[wave][mt * 4 + r][lane] = part;
-      }
-    __syncthreads();
-    // full scores: own half + partner half (a + b == b + a, so both waves of
-    // the pair hold identical scores); absent slots get -inf by adding it
-    float pv[2][4];
-    float lmx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sfull = xch[wave][mt * 4 + r][lane] + xch[wave ^ 4][mt * 4 + r][lane];
-        const int j = mt * 16 + 4 * g + r;
-        const float off = ((valid >> j) & 1u) ? 0.0f : -INFINITY;
-        pv[mt][r] = fmaf(sfull, p.scale_log2, off);
-        lmx = fmaxf(lmx, pv[mt][r]);
-      }
-
-    // ---- online softmax with a lazily raised reference max: O is rescaled
-    // only in the rare step where a score of a head exceeds its reference
-    // max by more than kLazy; l is kept per lane and summed at the end
-    if (__builtin_amdgcn_ballot_w64(lmx > m + kLazy) != 0) {
-      float mx = lmx;
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool upd = mx > m + kLazy;        // same in the head's 4 lanes
-      const float alpha = upd ? exp2f(m - mx) : 1.0f;   // m = -inf -> 0
-      if (upd) m = mx;
-      l *= alpha;
-      float al[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 4 * g + r);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[nt][r] *= al[r];
-    }
-    // exponents are at most kLazy; weights below 2^-126 may flush to zero
-    const float m_use = m == -INFINITY ? 0.0f : m;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[mt][r] = __builtin_amdgcn_exp2f(pv[mt][r] - m_use);
-        l += pv[mt][r];
-      }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- P . V over this wave's two value blocks; for an fp8 cache P
-    // carries the slot's scale of the block. The B fragments of tile j+1 are
-    // read while tile j is multiplied.
-    auto vfrag = [&](int vb, int j) {
-      const uint8_t* src = kt + (4 * g + (c >> 2)) * kKsRow + (vb * 128 + j * 16 + 4 * (c & 3)) * 2;
+    // V as the B operand: lane (dim, kg) needs the same slots of one value
+    // dim; two transposing reads of 4 slot rows each. In each 16-lane group
+    // (kg = group / 2, dims 16*(group % 2)..), source lane s points at slot
+    // row base + s/4 and dims +4(s%4).
+    const uint8_t* vbase = ktp + (4 * kg + (sl >> 2)) * kKsRow +
+                           (dw * 256 + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
+    auto vfrag = [&](int q) {
+      const uint8_t* src = vbase + 16 * (q / ND) * kKsRow + (q % ND) * 64;
       const v4i16 b0 = read_tr(src);
-      const v4i16 b1 = read_tr(src + 16 * kKsRow);
+      const v4i16 b1 = read_tr(src + 8 * kKsRow);
       const v4i16 bb[2] = {b0, b1};
       return *reinterpret_cast<const bf16x8*>(bb);
     };
-    bf16x8 vf[2];
-    vf[0] = vfrag(dw * 2, 0);
+    // exchanged partial scores of step k-1 and the slot bias
+    float4 xa[4], xb[4], bi[4];
 #pragma unroll
-    for (int vh = 0; vh < 2; ++vh) {
-      const int vb = dw * 2 + vh;
-      bf16x8 pa;
-      {
-        float q8[2][4];
+    for (int j = 0; j < 4; ++j) {
+      xa[j] = *reinterpret_cast<const float4*>(&xch[xp][wave][j][lane][0]);
+      xb[j] = *reinterpret_cast<const float4*>(&xch[xp][wave ^ 2][j][lane][0]);
+      bi[j] = *reinterpret_cast<const float4*>(bsp + 8 * j + 4 * kg);
+    }
+    bf16x8 fr[kRing], vf[kRing];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+    for (int i = 0; i < kPf; ++i) { fr[i] = kfrag(i); vf[i] = vfrag(i); }
+    f32x16 acc;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float s = 1.0f;
-            if constexpr (FP8) s = sc[(mt * 16 + 4 * g + r) * 4 + vb];
-            q8[mt][r] = pv[mt][r] * s;
-          }
-        const uint4 u = make_uint4(pack_bf16x2_hw(q8[0][0], q8[0][1]), pack_bf16x2_hw(q8[0][2], q8[0][3]),
-                                   pack_bf16x2_hw(q8[1][0], q8[1][1]), pack_bf16x2_hw(q8[1][2], q8[1][3]));
-        pa = *reinterpret_cast<const bf16x8*>(&u);
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    float sc[16];
+    float lmx = -INFINITY, m_use = 0.0f;
+    bf16x8 pa[2];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      if (g < KS) {
+        if (g + kPf < KS) fr[(g + kPf) % kRing] = kfrag(g + kPf);
+        if (g > 0) asm volatile("" ::"v"(fr[(g - 1) % kRing]));
       }
+      const int q = g - kPv0;
+      if (q >= 0) {
+        if (q + kPf < 2 * ND) vf[(q + kPf) % kRing] = vfrag(q + kPf);
+        if (q > 0) asm volatile("" ::"v"(vf[(q - 1) % kRing]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (g < KS) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[g % kRing], qb[g], acc, 0, 0, 0);
+      if (q >= 0)
+        o[q % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[q / ND], vf[q % kRing], o[q % ND], 0, 0, 0);
+      if (g < 2) {
+        // full scores of step k-1, 8 per group: own half + partner half
+        // (a + b == b + a, so both waves of the pair hold identical scores),
+        // scaled, plus the bias
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = vh * 8 + j;             // tile index within the wave
-        if (q + 1 < NT) vf[(q + 1) & 1] = vfrag(dw * 2 + (q + 1) / 8, (q + 1) % 8);
-        __builtin_amdgcn_sched_barrier(0);
-        o[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vf[q & 1], o[q], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 2 * g; j < 2 * g + 2; ++j) {
+          sc[4 * j] = fmaf(xa[j].x + xb[j].x, p.scale_log2, bi[j].x);
+          sc[4 * j + 1] = fmaf(xa[j].y + xb[j].y, p.scale_log2, bi[j].y);
+          sc[4 * j + 2] = fmaf(xa[j].z + xb[j].z, p.scale_log2, bi[j].z);
+          sc[4 * j + 3] = fmaf(xa[j].w + xb[j].w, p.scale_log2, bi[j].w);
+          lmx = fmaxf(lmx, fmaxf(fmaxf(sc[4 * j], sc[4 * j + 1]), fmaxf(sc[4 * j + 2], sc[4 * j + 3])));
+        }
+        if (g == 1) {
+          mall = fmaxf(mall, lmx);
+          const float hmx = fmaxf(lmx, __shfl_xor(lmx, 32));   // head c32 in both kg
+          m = m == -INFINITY ? hmx : m;                       // first step with a valid slot
+          ovf = ovf || lmx > m + kMaxExp;
+          m_use = m == -INFINITY ? 0.0f : m;
+        }
+      } else if (g < kPv0) {
+        // weights, 4 per group (a score beyond m + kMaxExp sets ovf and the
+        // pass is repeated, so its weight need not be finite)
+#pragma unroll
+        for (int e = 4 * (g - 2); e < 4 * (g - 1); ++e) {
+          sc[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+          l += sc[e];
+        }
+        if (g == kPv0 - 1) {
+          // P as the A operand for slot chunk ch (slots 16ch..16ch+15): lane
+          // (head c32, kg) holds slots 16ch + 4kg + {0..3, 8..11}
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+            const uint4 u = make_uint4(pack_bf16x2_hw(sc[8 * ch], sc[8 * ch + 1]),
+                                       pack_bf16x2_hw(sc[8 * ch + 2], sc[8 * ch + 3]),
+                                       pack_bf16x2_hw(sc[8 * ch + 4], sc[8 * ch + 5]),
+                                       pack_bf16x2_hw(sc[8 * ch + 6], sc[8 * ch + 7]));
+            pa[ch] = *reinterpret_cast<const bf16x8*>(&u);
+          }
+        }
+      } else if (g < kPv0 + 9) {
+        st.store_piece(ktn, bsn, tid, g - kPv0);
+      } else if (g >= KS) {
+        // exchange slice of S^T(k), one float4 per group
+        const int j = g - KS;
+        *reinterpret_cast<float4*>(&xch[xc][wave][j][lane][0]) =
+            make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+        if (g == kGroups - 1) st.load(p, ids + (k + 3) * kStep, tid);   // gather of step k+3
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  };
+
+  // partial scores of step 0 (prologue)
+  auto qk0 = [&]() {
+    f32x16 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[u][e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const bf16x8 f = *reinterpret_cast<const bf16x8*>(ks[0] + c32 * kKsRow + (kstep_of(i) * 16 + kg * 8) * 2);
+      acc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qb[i], acc[i & 1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(&xch[0][wave][j][lane][0]) =
+          make_float4(acc[0][4 * j] + acc[1][4 * j], acc[0][4 * j + 1] + acc[1][4 * j + 1],
+                      acc[0][4 * j + 2] + acc[1][4 * j + 2], acc[0][4 * j + 3] + acc[1][4 * j + 3]);
+  };
+  auto run_pass = [&]() {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[d][e] = 0.0f;
+    l = 0.0f;
+    if (nsteps > 0) {
+      StageF8 sa, sb;
+      sa.load(p, ids, tid);
+      sb.load(p, ids + kStep, tid);
+      sa.store(ks[0], bias[0], tid);
+      sa.load(p, ids + 2 * kStep, tid);
+      sb.store(ks[1], bias[1], tid);
+      sb.load(p, ids + 3 * kStep, tid);
+      __syncthreads();
+      qk0();
+      __syncthreads();
+      // steps past nsteps are empty (every bias is -inf): their P is zero
+      for (int k = 1; k <= nsteps; k += 2) {
+        iter(k, sa, 0, 1);
+        iter(k + 1, sb, 1, 0);
       }
     }
   };
 
-  if (nsteps > 0) {
-    StageW<FP8> sa, sb;
-    sa.load(p, ids, tid);
-    sb.load(p, ids + kStep, tid);
-    sa.store(ks[0], scl[0], tid);
-    sa.load(p, ids + 2 * kStep, tid);
+  __syncthreads();   // ids
+  m = -INFINITY;
+  mall = -INFINITY;
+  ovf = false;
+  run_pass();
+  // a score beyond the clamp anywhere in the block: run again with the true
+  // maximum as reference (both waves of a head group agree on m and mall)
+  if (tid == 0) s_ovf = 0;
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(ovf) != 0 && lane == 0) s_ovf = 1;
+  __syncthreads();
+  if (s_ovf != 0) {
+    m = fmaxf(mall, __shfl_xor(mall, 32));
+    ovf = false;
     __syncthreads();
-    for (int s = 0; s < nsteps; s += 2) {
-      sb.store(ks[1], scl[1], tid);                 // step s + 1
-      sb.load(p, ids + (s + 3) * kStep, tid);       // step s + 3
-      __builtin_amdgcn_sched_barrier(0);
-      compute(ks[0], scl[0], vmask[s]);
-      __syncthreads();
-      sa.store(ks[0], scl[0], tid);                 // step s + 2
-      sa.load(p, ids + (s + 4) * kStep, tid);       // step s + 4
-      __builtin_amdgcn_sched_barrier(0);
-      compute(ks[1], scl[1], vmask[s + 1]);         // empty when s + 1 == nsteps
-      __syncthreads();
-    }
+    run_pass();
   }
 
-  // ---- finalize: lane (dim c of tile nt, group g) holds O[head 4g+r][dim]
-  l += __shfl_xor(l, 16);
+  // ---- finalize: lane (dim c32 of tile d, group kg) element e holds
+  // O[head 8(e/4) + 4kg + e%4][dim]
   l += __shfl_xor(l, 32);
-  float lr[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) lr[r] = __shfl(l, 4 * g + r);
   const float lse_val = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-  const int d0 = dw * (kDV / 2);
-  if (p.n_splits == 1) {
+  const int d0 = dw * 256;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+  for (int e = 0; e < 16; ++e) {
+    const int hr = 8 * (e >> 2) + 4 * kg + (e & 3);
+    const float lr = __shfl(l, hr);
+    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+    if (p.n_splits == 1) {
+      uint16_t* orow = p.out + (t * p.H + h0 + hr) * kDV + d0 + c32;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = lr[r] > 0.0f ? o[nt][r] / lr[r] : 0.0f;
-        p.out[(t * p.H + h0 + 4 * g + r) * kDV + d0 + nt * 16 + c] = (uint16_t)f32_to_bf16_bits(v);
-      }
-    if (p.lse && dw == 0 && g == 0) p.lse[t * p.H + h0 + c] = lse_val;
-  } else {
-    const int64_t base = ((int64_t)split * p.T + t) * p.H;
+      for (int d = 0; d < ND; ++d) orow[d * 32] = (uint16_t)f32_to_bf16_bits(o[d][e] * inv);
+    } else {
+      float* orow = p.ws_o + (((int64_t)split * p.T + t) * p.H + h0 + hr) * kDV + d0 + c32;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = lr[r] > 0.0f ? o[nt][r] / lr[r] : 0.0f;
-        p.ws_o[(base + h0 + 4 * g + r) * kDV + d0 + nt * 16 + c] = v;
-      }
-    if (dw == 0 && g == 0) p.ws_lse[base + h0 + c] = lse_val;
+      for (int d = 0; d < ND; ++d) orow[d * 32] = o[d][e] * inv;
+    }
+  }
+  if (dw == 0 && kg == 0) {
+    if (p.n_splits == 1) {
+      if (p.lse) p.lse[t * p.H + h0 + c32] = lse_val;
+    } else {
+      p.ws_lse[((int64_t)split * p.T + t) * p.H + h0 + c32] = lse_val;
+    }
   }
 }
 
@@ -884,12 +918,12 @@ struct Plan {
   int nh, hw, hb_heads, n_hb, n_splits, split_slots;
 };
 
-// Heads per block and KV splits: the 64-head kernel runs one block per CU,
-// so it aims at 256 blocks (one per CU) and at most kMaxSplit slots per
-// block; the narrower kernel runs two blocks per CU.
-Plan make_plan(int T, int H, int topk, bool decode) {
+// Heads per block and KV splits: the 64-head kernel (fp8 caches) runs one
+// block per CU, so it aims at 256 blocks (one per CU) and at most kMaxSplit
+// slots per block; the narrower kernel runs two blocks per CU.
+Plan make_plan(int T, int H, int topk, bool decode, bool fp8) {
   Plan pl;
-  pl.wide = H % 64 == 0;
+  pl.wide = fp8 && H % 64 == 0;
   if (pl.wide) { pl.nh = 1; pl.hw = 4; }
   else if (H % 32 == 0) { pl.nh = 1; pl.hw = 2; }
   else { pl.nh = 1; pl.hw = 1; }
@@ -952,7 +986,8 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
                       num_slots, indices, idx_stride, T, H, topk, d_qk, d_v, out);
   if (st != NSA_OK) return st;
   if (T == 0) return nsa::ok();
-  const Plan pl = make_plan(T, H, topk, decode);
+  const bool fp8 = kv_dtype == NSA_KV_FP8_656;
+  const Plan pl = make_plan(T, H, topk, decode, fp8);
   const size_t need = workspace_bytes(pl, T, H);
   NSA_REQUIRE(need == 0 || (workspace && ws_bytes >= need), NSA_ERR_WORKSPACE,
               "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
@@ -983,7 +1018,6 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
   const int64_t blocks = (int64_t)T * pl.n_hb * pl.n_splits;
   NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: grid too large", fn);
   hipStream_t s = (hipStream_t)stream;
-  const bool fp8 = kv_dtype == NSA_KV_FP8_656;
   const dim3 grid((unsigned)blocks), block(pl.wide ? kThreadsW : kThreads);
 #define NSA_MLA_LAUNCH(NH, HW)                                                      \
   do {                                                                            \
@@ -991,8 +1025,7 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
     else hipLaunchKernelGGL((sparse_mla_kernel<NH, HW, false>), grid, block, 0, s, p);    \
   } while (0)
   if (pl.wide) {
-    if (fp8) hipLaunchKernelGGL(sparse_mla_h64_kernel<true>, grid, block, 0, s, p);
-    else hipLaunchKernelGGL(sparse_mla_h64_kernel<false>, grid, block, 0, s, p);
+    hipLaunchKernelGGL(sparse_mla_h64_kernel, grid, block, 0, s, p);
   } else if (pl.hw == 2) {
     NSA_MLA_LAUNCH(1, 2);
   } else {
@@ -1015,10 +1048,15 @@ extern "C" int nsa_sparse_mla_workspace_size(int T, int H, int topk, int d_v,
               "nsa_sparse_mla_workspace_size: null output");
   NSA_REQUIRE(T >= 0 && H > 0 && H % 16 == 0 && topk > 0 && d_v == kDV,
               NSA_ERR_INVALID_ARG, "nsa_sparse_mla_workspace_size: bad sizes");
-  // the larger of the decode and extend plans, so one buffer serves both
-  const Plan a = make_plan(T, H, topk, true), b = make_plan(T, H, topk, false);
-  const size_t wa = workspace_bytes(a, T, H), wb = workspace_bytes(b, T, H);
-  *bytes = wa > wb ? wa : wb;
+  // the largest of the decode and extend plans for either cache format, so
+  // one buffer serves every call
+  size_t w = 0;
+  for (int dec = 0; dec < 2; ++dec)
+    for (int f8 = 0; f8 < 2; ++f8) {
+      const size_t b = workspace_bytes(make_plan(T, H, topk, dec != 0, f8 != 0), T, H);
+      w = b > w ? b : w;
+    }
+  *bytes = w;
   return nsa::ok();
 }
 
