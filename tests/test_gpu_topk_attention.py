@@ -180,3 +180,27 @@ def test_sparse_mla_strided_q_and_determinism():
                                                   CacheFromRows(dict(enumerate(vals))),
                                                   idx, 0.07)
     check_attention(a.float().cpu().numpy(), la.cpu().numpy(), o_ref, lse_ref, "bf16")
+
+
+def test_sparse_mla_score_jump_reruns_exactly():
+    """Scores of a later step far above the first step's (exp2 of the scaled
+    difference, about 332, overflows fp32): the 64-head fp8 kernel must
+    still match the oracle (it runs the split again with the true maximum)."""
+    nsa = need_gpu()
+    T, H, topk = 2, 64, 64
+    q = torch.ones(T, H, 576, dtype=torch.bfloat16)
+    kv = torch.zeros(64, 576, dtype=torch.bfloat16)
+    kv[32:] = 0.1                                    # second step: q.k = 57.6
+    bits = kv.view(torch.int16).numpy().view(np.uint16)
+    raw = oracle.quant.quantize_k_cache(bits)
+    vals = oracle.quant.dequantize_rows(raw)
+    idx = np.tile(np.arange(64), (T, 1))
+    idx[1] = idx[1][::-1]                            # large scores first
+    out, lse = nsa.nsa_sparse_mla_decode(q.to(DEV), torch.as_tensor(raw, device=DEV),
+                                         nsa.KV_FP8_656,
+                                         torch.as_tensor(idx, dtype=torch.int32, device=DEV),
+                                         4.0)
+    o_ref, lse_ref = oracle.sparse_mla.sparse_mla(q.to(torch.float64).numpy(),
+                                                  CacheFromRows(dict(enumerate(vals))),
+                                                  idx, 4.0)
+    check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "fp8")
