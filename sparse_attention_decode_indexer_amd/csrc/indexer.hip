@@ -11,7 +11,9 @@
 // fp8 path (Hi = 64 heads, Di = 128), MI355X design:
 //   * one block of 4 waves per (row, chunk of 32 pages); wave w takes pages
 //     w, w+4, ... of the chunk, so a wave always works on a whole page
-//     (64 tokens = 8 KB of keys + 256 B of scales, contiguous);
+//     (64 tokens = 8 KB of keys + 256 B of scales, contiguous); two page
+//     buffers per wave keep the register count at 140 (three waves per
+//     SIMD), which measured faster than deeper prefetch at lower occupancy;
 //   * v_mfma_f32_16x16x128_f8f6f4 with A = 16 heads x 128 dims of q (held in
 //     registers for the whole block) and B = 128 dims x 16 tokens of keys, so
 //     the dot products over all 128 dims take one instruction and the output
@@ -20,8 +22,8 @@
 //     16 in-lane FMAs plus a 3-shuffle transpose-reduce that leaves token
 //     lane in lane `lane`, so each page is stored as 64 consecutive floats;
 //   * keys are loaded straight from HBM with 16-byte loads (each instruction
-//     reads 64 contiguous bytes of 16 key rows), the next page's loads are
-//     issued before the current page's MFMAs.
+//     reads 64 contiguous bytes of 16 key rows); the next page is in flight
+//     while one is scored, and no load sits under a branch.
 // The contraction dimension is split over lanes identically for q and for
 // the keys (each lane takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of a
 // 128-byte row, g = lane / 16), so the dot products do not depend on the
@@ -35,7 +37,7 @@ constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kPageBytesFp8 = kPage * kDim + kPage * 4;  // 8448
 constexpr int kWaves = 4;
-constexpr int kPagesPerBlock = 64;
+constexpr int kPagesPerBlock = 32;
 
 // Logical block id such that consecutive ids run on the same XCD (work
 // groups are dealt to the 8 XCDs round-robin).
@@ -46,10 +48,14 @@ __device__ __forceinline__ uint32_t xcd_logical_block(uint32_t bid, uint32_t n) 
 
 struct PageKeys {
   i32x8 k[4];  // 4 tiles of 16 tokens
+  float ks;    // scale of token `lane`
 };
 
+// Keys of one page for this lane plus the scale of token `lane`. Always
+// issued (an absent page reads page 0 and its results are masked): a load
+// under a branch would make the compiler wait for every load in flight.
 __device__ __forceinline__ void load_page(PageKeys& pk, const uint8_t* base,
-                                          int c, int g) {
+                                          int c, int g, int lane) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint8_t* row = base + (j * 16 + c) * kDim;
@@ -58,6 +64,7 @@ __device__ __forceinline__ void load_page(PageKeys& pk, const uint8_t* base,
     pk.k[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
+  pk.ks = *reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane);
 }
 
 __global__ void __launch_bounds__(256)
@@ -111,58 +118,47 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
   const int np_w = (p_end - first + kWaves - 1) / kWaves;
   const int id_lane = lane < np_w ? prow[first + kWaves * lane] : -1;
 
-  auto page_id = [&](int i) -> int {
+  auto page_id = [&](int i) -> int {   // -1: absent or invalid
     const int id = __builtin_amdgcn_readlane(id_lane, i);
     return (id >= 0 && id < num_pages) ? id : -1;
   };
   auto fetch = [&](PageKeys& pk, int i) {
     const int id = page_id(i);
-    if (id >= 0) load_page(pk, cache + (int64_t)id * kPageBytesFp8, c, g);
+    load_page(pk, cache + (int64_t)(id >= 0 ? id : 0) * kPageBytesFp8, c, g, lane);
   };
   auto score = [&](const PageKeys& pk, int i) {
-    const int id = page_id(i);
-    float result = -INFINITY;
-    if (id >= 0) {
-      const uint8_t* base = cache + (int64_t)id * kPageBytesFp8;
-      const float ks = *reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane);
-      float v[4];
+    float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float s = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      float s = 0.0f;
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
-          const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              qa[ht], pk.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      for (int ht = 0; ht < 4; ++ht) {
+        const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            qa[ht], pk.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) s = fmaf(wr[ht][r], fmaxf(acc[r], 0.0f), s);
-        }
-        v[j] = s;
+        for (int r = 0; r < 4; ++r) s = fmaf(wr[ht][r], fmaxf(acc[r], 0.0f), s);
       }
-      // transpose-reduce over the 4 lane groups: group g keeps tile g
-      const bool b0 = g & 1, b1 = (g >> 1) & 1;
-      const float u0 = (b0 ? v[1] : v[0]) + __shfl_xor(b0 ? v[0] : v[1], 16);
-      const float u1 = (b0 ? v[3] : v[2]) + __shfl_xor(b0 ? v[2] : v[3], 16);
-      const float tot = (b1 ? u1 : u0) + __shfl_xor(b1 ? u0 : u1, 32);
-      result = tot * ks;  // position (first + 4 i) * 64 + lane
+      v[j] = s;
     }
-    const int s = (first + kWaves * i) * kPage + lane;
-    if (s < L) lrow[s] = result;
+    // transpose-reduce over the 4 lane groups: group g keeps tile g
+    const bool b0 = g & 1, b1 = (g >> 1) & 1;
+    const float u0 = (b0 ? v[1] : v[0]) + __shfl_xor(b0 ? v[0] : v[1], 16);
+    const float u1 = (b0 ? v[3] : v[2]) + __shfl_xor(b0 ? v[2] : v[3], 16);
+    const float tot = (b1 ? u1 : u0) + __shfl_xor(b1 ? u0 : u1, 32);
+    const float result = page_id(i) >= 0 ? tot * pk.ks : -INFINITY;
+    const int s = (first + kWaves * i) * kPage + lane;   // position of token `lane`
+    if (i < np_w && s < L) lrow[s] = result;
   };
 
-  // three page buffers: keys of pages i+1 and i+2 are in flight while page i
-  // is scored
-  PageKeys b0, b1, b2;
+  // two page buffers: the keys of page i+1 are in flight while page i is
+  // scored; a fetch past the wave's pages reads page 0 and is not stored
+  PageKeys b0, b1;
   fetch(b0, 0);
-  if (1 < np_w) fetch(b1, 1);
-  for (int i = 0; i < np_w; i += 3) {
-    if (i + 2 < np_w) fetch(b2, i + 2);
+  for (int i = 0; i < np_w; i += 2) {
+    fetch(b1, i + 1);
     score(b0, i);
-    if (i + 1 >= np_w) break;
-    if (i + 3 < np_w) fetch(b0, i + 3);
+    fetch(b0, i + 2);
     score(b1, i + 1);
-    if (i + 2 >= np_w) break;
-    if (i + 4 < np_w) fetch(b1, i + 4);
-    score(b2, i + 2);
   }
 }
 
