@@ -36,16 +36,25 @@ __device__ __forceinline__ int q_rows_of(int mode, int draft,
   return extend_lens[i];
 }
 
-__device__ long long block_sum(long long v, long long* red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
+// Block-wide sums of three values: wave reductions with shuffles, then one
+// exchange through LDS.
+__device__ void block_sum3(long long& a, long long& b, long long& c, long long* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o);
+    b += __shfl_xor(b, o);
+    c += __shfl_xor(c, o);
   }
-  long long r = red[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[3 * wave] = a; red[3 * wave + 1] = b; red[3 * wave + 2] = c; }
   __syncthreads();
-  return r;
+  a = b = c = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {   // fixed order: every thread gets the same sums
+    a += red[3 * w];
+    b += red[3 * w + 1];
+    c += red[3 * w + 2];
+  }
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -62,7 +71,7 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
                       int32_t* real_page_table, int64_t rpt_stride,
                       int32_t* token_to_req, int32_t* page_table_1,
                       int64_t pt1_stride) {
-  __shared__ long long red[kThreads];
+  __shared__ long long red[3 * (kThreads / 64)];
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int d = (mode == NSA_MODE_TARGET_VERIFY) ? draft : 0;
@@ -77,9 +86,7 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
     pq += ql;
     pn += clipped_sum(kv - ql + 1, ql, topk);
   }
-  pk = block_sum(pk, red);
-  pq = block_sum(pq, red);
-  pn = block_sum(pn, red);
+  block_sum3(pk, pq, pn, red);
 
   if (r == 0 && tid == 0) {
     cu_seqlens_k[0] = 0;
@@ -114,8 +121,22 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
   const int32_t* row = req_to_token + (int64_t)req_pool_indices[r] * rtt_stride;
   const int ncols = (max_seqlen_k + NSA_PAGE_SIZE - 1) / NSA_PAGE_SIZE;
   int32_t* rpt = real_page_table + (int64_t)r * rpt_stride;
-  for (int p = tid; p < ncols; p += kThreads)
-    rpt[p] = row[(int64_t)p * NSA_PAGE_SIZE] >> 6;
+  // strided gather (one cache line per entry): up to 8 loads in flight per
+  // thread, all issued before any is stored
+  constexpr int kBatch = 8;
+  for (int p0 = 0; p0 < ncols; p0 += kThreads * kBatch) {
+    int32_t v[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int p = p0 + b * kThreads + tid;
+      v[b] = row[(int64_t)min(p, ncols - 1) * NSA_PAGE_SIZE];
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int p = p0 + b * kThreads + tid;
+      if (p < ncols) rpt[p] = v[b] >> 6;
+    }
+  }
   if (page_table_1 != nullptr) {
     int32_t* pt = page_table_1 + (int64_t)r * pt1_stride;
     for (int c = tid; c < max_seqlen_k; c += kThreads) pt[c] = row[c];
