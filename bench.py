@@ -191,6 +191,8 @@ def main():
     logits = torch.empty(T, nsa.logits_row_stride(w.max_seqlen_k),
                          dtype=torch.float32, device=dev)
     slots = torch.empty(T, w.topk, dtype=i32, device=dev)
+    # top-k histogram counted by the indexer; the top-k clears it after use
+    key_hist = nsa.new_key_hist(T, dev) if idt == nsa.DTYPE_FP8_E4M3 else None
     out = torch.empty(T, w.heads, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(T, w.heads, dtype=torch.float32, device=dev)
     ws = torch.empty(max(nsa.sparse_mla_workspace_size(T, w.heads, w.topk), 16),
@@ -209,11 +211,12 @@ def main():
         nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
                                md["real_page_table"], md["token_to_req"],
                                md["seqlens_expanded"], w.max_seqlen_k,
-                               logits=logits, dtype=idt)
+                               logits=logits, dtype=idt, key_hist=key_hist)
         if e: e[2].record()
         nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                w.max_seqlen_k, table=md["real_page_table"],
-                               token_to_req=md["token_to_req"], out=slots)
+                               token_to_req=md["token_to_req"], out=slots,
+                               key_hist=key_hist)
         if e: e[3].record()
         attn(w.q, cache, kvd, slots, w.sm_scale, md["nsa_cache_seqlens"],
              out=out, lse=lse, workspace=ws)

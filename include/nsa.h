@@ -185,6 +185,43 @@ int nsa_topk_transform(const float* logits, int64_t logits_stride,
                        int page_size, int32_t* out, int64_t out_stride,
                        void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- f1: the top-k histogram fused into the indexer ----------------------------
+ * Direction of the pages' folded top-k plan ("dsa_backend.py (sglang main)",
+ * _build_topk_v2_plan: top-k work prepared from the same lengths the
+ * transform receives): the indexer, which holds every logit anyway, also
+ * histograms them, so the top-k reads the logits once instead of twice.
+ *
+ * nsa_indexer_logits_hist: as nsa_indexer_logits (fp8 path only), and adds
+ * to key_hist[t * 4096 + b] the number of positions s < min(L_t,
+ * max_seqlen_k) whose logit's order key has top 12 bits b. The order key of
+ * x: NaN -> 0; -0 -> +0; otherwise the fp32 bits with the sign bit set for
+ * x >= 0 and all bits inverted for x < 0 (so keys order as the floats).
+ * key_hist is device memory of T * 4096 uint32, 4-byte aligned, owned by the
+ * caller, and must hold zeros on entry (counts are added atomically).
+ *
+ * nsa_topk_transform_hist: as nsa_topk_transform, with key_hist from
+ * nsa_indexer_logits_hist over the same logits (16-byte aligned); it needs
+ * no workspace. It sets rows 0..T-1 of key_hist back to zero, so one buffer
+ * serves every layer. A row whose counts do not add up to its length takes
+ * a slower exact path; any other mismatch between key_hist and the logits is
+ * the caller's contract (the result is then unspecified but stays in the
+ * bounds of `out`).
+ */
+int nsa_indexer_logits_hist(const void* q, int q_dtype, const float* weights,
+                            const void* k_index_cache, int k_dtype,
+                            int64_t num_pages, const int32_t* real_page_table,
+                            int64_t rpt_stride, const int32_t* token_to_req,
+                            const int32_t* seqlens_expanded, int T, int Hi,
+                            int Di, int page_size, int max_seqlen_k,
+                            float* logits, int64_t logits_stride,
+                            uint32_t* key_hist, void* stream);
+int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
+                            const int32_t* lengths, int T, int topk,
+                            int max_seqlen_k, const int32_t* table,
+                            int64_t table_stride, const int32_t* token_to_req,
+                            int page_size, uint32_t* key_hist, int32_t* out,
+                            int64_t out_stride, void* stream);
+
 /* ---- a3: page-table transform ---------------------------------------------------
  * [nsa-fork] forward_decode / forward_extend:
  * transform_index_page_table_decode / _prefill(page_table_1, topk_indices,

@@ -93,12 +93,22 @@ def logits_row_stride(max_seqlen_k):
     return max(64, (max_seqlen_k + 63) // 64 * 64)
 
 
+KEY_BINS = 4096
+
+
+def new_key_hist(T, device):
+    """A zeroed [T, 4096] key histogram (int32 storage of uint32 counts) for
+    the fused indexer / top-k pair; the top-k clears it again after use."""
+    return torch.zeros(T, KEY_BINS, dtype=torch.int32, device=device)
+
+
 def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits=None,
-                       dtype=DTYPE_FP8_E4M3):
+                       dtype=DTYPE_FP8_E4M3, key_hist=None):
     """Indexer logits [T, >= max_seqlen_k] fp32 (positions past each row's
     length are left unwritten). ``q``: [T, Hi, Di] uint8 fp8 codes (dtype
-    DTYPE_FP8_E4M3) or float32 (DTYPE_FP32)."""
+    DTYPE_FP8_E4M3) or float32 (DTYPE_FP32). With ``key_hist`` (zeroed, see
+    new_key_hist) the logits' top-k histogram is counted in the same pass."""
     _check(q, "q", torch.uint8 if dtype == DTYPE_FP8_E4M3 else torch.float32, 3)
     _check(weights, "weights", torch.float32, 2)
     _check(index_cache, "index_cache", torch.uint8, 2)
@@ -110,18 +120,26 @@ def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
         logits = torch.empty(T, logits_row_stride(max_seqlen_k),
                              dtype=torch.float32, device=q.device)
     _check(logits, "logits", torch.float32, 2, contiguous=False)
-    call("nsa_indexer_logits", _ptr(q), dtype, _ptr(weights), _ptr(index_cache),
-         dtype, index_cache.shape[0], _ptr(real_page_table),
-         real_page_table.stride(0), _ptr(token_to_req), _ptr(seqlens_expanded),
-         T, Hi, Di, PAGE_SIZE, max_seqlen_k, _ptr(logits), logits.stride(0),
-         _stream())
+    args = (_ptr(q), dtype, _ptr(weights), _ptr(index_cache), dtype,
+            index_cache.shape[0], _ptr(real_page_table), real_page_table.stride(0),
+            _ptr(token_to_req), _ptr(seqlens_expanded), T, Hi, Di, PAGE_SIZE,
+            max_seqlen_k, _ptr(logits), logits.stride(0))
+    if key_hist is None:
+        call("nsa_indexer_logits", *args, _stream())
+    else:
+        _check(key_hist, "key_hist", torch.int32, 2)
+        if key_hist.shape[0] < T or key_hist.shape[1] != KEY_BINS:
+            raise ValueError("key_hist must be [>= T, 4096]")
+        call("nsa_indexer_logits_hist", *args, _ptr(key_hist), _stream())
     return logits
 
 
 def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
-                       token_to_req=None, out=None):
+                       token_to_req=None, out=None, key_hist=None):
     """Top-k positions per row (ascending position order, -1 padded), or
-    physical slots when ``table`` (the compact page table) is given."""
+    physical slots when ``table`` (the compact page table) is given. With
+    ``key_hist`` (filled by nsa_indexer_logits on the same logits) the logits
+    are read once and key_hist is cleared for reuse."""
     _check(lengths, "lengths", torch.int32, 1)
     T = lengths.numel()
     if logits is not None:
@@ -132,6 +150,16 @@ def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
     if out is None:
         out = torch.empty(T, topk, dtype=torch.int32, device=lengths.device)
     _check(out, "out", torch.int32, 2, contiguous=False)
+    if key_hist is not None:
+        _check(key_hist, "key_hist", torch.int32, 2)
+        if key_hist.shape[0] < T or key_hist.shape[1] != KEY_BINS:
+            raise ValueError("key_hist must be [>= T, 4096]")
+        call("nsa_topk_transform_hist", _ptr(logits),
+             logits.stride(0) if logits is not None else 0, _ptr(lengths), T, topk,
+             max_seqlen_k, _ptr(table), table.stride(0) if table is not None else 0,
+             _ptr(token_to_req), PAGE_SIZE, _ptr(key_hist), _ptr(out), out.stride(0),
+             _stream())
+        return out
     ws = ctypes.c_size_t(0)
     call("nsa_topk_workspace_size", T, max_seqlen_k, topk, ctypes.byref(ws))
     work = (torch.empty(ws.value, dtype=torch.uint8, device=lengths.device)

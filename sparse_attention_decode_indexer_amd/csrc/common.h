@@ -61,6 +61,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Order-preserving image of a float in uint32: NaN ranks lowest and -0.0
+// equals +0.0 (so equal values tie and are broken by position). The top-k
+// histograms count its top 12 bits (kKeyBins bins).
+constexpr int kKeyBins = 4096;
+__device__ __forceinline__ uint32_t order_key(float x) {
+  if (x != x) return 0u;
+  const uint32_t u = x == 0.0f ? 0u : __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 

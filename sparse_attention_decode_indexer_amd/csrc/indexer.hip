@@ -67,6 +67,10 @@ __device__ __forceinline__ void load_page(PageKeys& pk, const uint8_t* base,
   pk.ks = *reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane);
 }
 
+// HIST: also count the top 12 bits of every written logit's order key into
+// key_hist[t][0..4095] (an LDS histogram per block, then one global atomic
+// per nonzero bin), so the top-k needs no pass of its own to histogram.
+template <bool HIST>
 __global__ void __launch_bounds__(256)
 indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    const uint8_t* __restrict__ cache, int64_t num_pages,
@@ -74,7 +78,8 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    const int32_t* __restrict__ t2r,
                    const int32_t* __restrict__ seqlens, int max_seqlen_k,
                    float* __restrict__ logits, int64_t logits_stride,
-                   int chunks_per_row) {
+                   int chunks_per_row, uint32_t* __restrict__ key_hist) {
+  __shared__ uint32_t lhist[HIST ? kKeyBins : 1];
   const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int64_t t = lb / chunks_per_row;
   const int chunk = lb % chunks_per_row;
@@ -111,11 +116,16 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
   const int32_t* prow = rpt + (int64_t)t2r[t] * rpt_stride;
   float* lrow = logits + t * logits_stride;
 
-  // this wave's pages: p_begin + wave + 4 i, i < np_w (at most 16); lane i
+  if constexpr (HIST) {
+    uint4* z = reinterpret_cast<uint4*>(lhist);
+    for (int i = threadIdx.x; i < kKeyBins / 4; i += 256) z[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+  }
+
+  // this wave's pages: p_begin + wave + 4 i, i < np_w (at most 8); lane i
   // holds the id of the i-th one, so no key load waits on an id load
   const int first = p_begin + wave;
-  if (first >= p_end) return;
-  const int np_w = (p_end - first + kWaves - 1) / kWaves;
+  const int np_w = first < p_end ? (p_end - first + kWaves - 1) / kWaves : 0;
   const int id_lane = lane < np_w ? prow[first + kWaves * lane] : -1;
 
   auto page_id = [&](int i) -> int {   // -1: absent or invalid
@@ -147,18 +157,35 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
     const float tot = (b1 ? u1 : u0) + __shfl_xor(b1 ? u0 : u1, 32);
     const float result = page_id(i) >= 0 ? tot * pk.ks : -INFINITY;
     const int s = (first + kWaves * i) * kPage + lane;   // position of token `lane`
-    if (i < np_w && s < L) lrow[s] = result;
+    if (i < np_w && s < L) {
+      lrow[s] = result;
+      if constexpr (HIST) atomicAdd(&lhist[order_key(result) >> 20], 1u);
+    }
   };
 
   // two page buffers: the keys of page i+1 are in flight while page i is
   // scored; a fetch past the wave's pages reads page 0 and is not stored
-  PageKeys b0, b1;
-  fetch(b0, 0);
-  for (int i = 0; i < np_w; i += 2) {
-    fetch(b1, i + 1);
-    score(b0, i);
-    fetch(b0, i + 2);
-    score(b1, i + 1);
+  if (np_w > 0) {
+    PageKeys b0, b1;
+    fetch(b0, 0);
+    for (int i = 0; i < np_w; i += 2) {
+      fetch(b1, i + 1);
+      score(b0, i);
+      fetch(b0, i + 2);
+      score(b1, i + 1);
+    }
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* dst = key_hist + t * kKeyBins;
+    const uint4* h4 = reinterpret_cast<const uint4*>(lhist);
+    for (int i = threadIdx.x; i < kKeyBins / 4; i += 256) {
+      const uint4 v = h4[i];
+      if (v.x) atomicAdd(&dst[4 * i], v.x);
+      if (v.y) atomicAdd(&dst[4 * i + 1], v.y);
+      if (v.z) atomicAdd(&dst[4 * i + 2], v.z);
+      if (v.w) atomicAdd(&dst[4 * i + 3], v.w);
+    }
   }
 }
 
@@ -204,18 +231,15 @@ indexer_fp32_kernel(const float* __restrict__ q, const float* __restrict__ w,
 
 }  // namespace
 
-extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
-                                  const float* weights,
-                                  const void* k_index_cache, int k_dtype,
-                                  int64_t num_pages,
-                                  const int32_t* real_page_table,
-                                  int64_t rpt_stride,
-                                  const int32_t* token_to_req,
-                                  const int32_t* seqlens_expanded, int T,
-                                  int Hi, int Di, int page_size,
-                                  int max_seqlen_k, float* logits,
-                                  int64_t logits_stride, void* stream) {
-  const char* fn = "nsa_indexer_logits";
+namespace {
+
+int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights,
+                const void* k_index_cache, int k_dtype, int64_t num_pages,
+                const int32_t* real_page_table, int64_t rpt_stride,
+                const int32_t* token_to_req, const int32_t* seqlens_expanded,
+                int T, int Hi, int Di, int page_size, int max_seqlen_k,
+                float* logits, int64_t logits_stride, uint32_t* key_hist,
+                void* stream) {
   NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0 && num_pages >= 0,
               NSA_ERR_INVALID_ARG, "%s: negative size", fn);
   NSA_REQUIRE(page_size == NSA_PAGE_SIZE, NSA_ERR_UNSUPPORTED,
@@ -233,6 +257,8 @@ extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
                 NSA_ERR_UNSUPPORTED,
                 "%s: fp32 path needs 1 <= Hi <= 64, 4 <= Di <= 128, Di %% 4 == 0",
                 fn);
+  NSA_REQUIRE(key_hist == nullptr || fp8, NSA_ERR_UNSUPPORTED,
+              "%s: the fused histogram needs the fp8 path", fn);
   if (T == 0 || max_seqlen_k == 0) return nsa::ok();
   NSA_REQUIRE(q && weights && k_index_cache && real_page_table && token_to_req &&
                   seqlens_expanded && logits,
@@ -243,19 +269,21 @@ extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
   NSA_REQUIRE(rpt_stride >= ncols, NSA_ERR_INVALID_ARG,
               "%s: rpt_stride < ceil(max_seqlen_k/64)", fn);
   NSA_REQUIRE(nsa::aligned(q, 16) && nsa::aligned(weights, 16) &&
-                  nsa::aligned(k_index_cache, 16) && nsa::aligned(logits, 4),
+                  nsa::aligned(k_index_cache, 16) && nsa::aligned(logits, 4) &&
+                  nsa::aligned(key_hist, 4),
               NSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   hipStream_t s = (hipStream_t)stream;
   if (fp8) {
     const int chunks = (int)((ncols + kPagesPerBlock - 1) / kPagesPerBlock);
     const int64_t blocks = (int64_t)T * chunks;
     NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
-    hipLaunchKernelGGL(indexer_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0,
+    auto kern = key_hist ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0,
                        s, static_cast<const uint8_t*>(q), weights,
                        static_cast<const uint8_t*>(k_index_cache), num_pages,
                        real_page_table, rpt_stride, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits, logits_stride,
-                       chunks);
+                       chunks, key_hist);
   } else {
     const int chunks = (max_seqlen_k + 255) / 256;
     const int64_t blocks = (int64_t)T * chunks;
@@ -269,4 +297,44 @@ extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
                        Hi, Di, chunks);
   }
   return nsa::check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
+                                  const float* weights,
+                                  const void* k_index_cache, int k_dtype,
+                                  int64_t num_pages,
+                                  const int32_t* real_page_table,
+                                  int64_t rpt_stride,
+                                  const int32_t* token_to_req,
+                                  const int32_t* seqlens_expanded, int T,
+                                  int Hi, int Di, int page_size,
+                                  int max_seqlen_k, float* logits,
+                                  int64_t logits_stride, void* stream) {
+  return indexer_run("nsa_indexer_logits", q, q_dtype, weights, k_index_cache,
+                     k_dtype, num_pages, real_page_table, rpt_stride,
+                     token_to_req, seqlens_expanded, T, Hi, Di, page_size,
+                     max_seqlen_k, logits, logits_stride, nullptr, stream);
+}
+
+extern "C" int nsa_indexer_logits_hist(const void* q, int q_dtype,
+                                       const float* weights,
+                                       const void* k_index_cache, int k_dtype,
+                                       int64_t num_pages,
+                                       const int32_t* real_page_table,
+                                       int64_t rpt_stride,
+                                       const int32_t* token_to_req,
+                                       const int32_t* seqlens_expanded, int T,
+                                       int Hi, int Di, int page_size,
+                                       int max_seqlen_k, float* logits,
+                                       int64_t logits_stride, uint32_t* key_hist,
+                                       void* stream) {
+  const char* fn = "nsa_indexer_logits_hist";
+  NSA_REQUIRE(T == 0 || key_hist != nullptr, NSA_ERR_INVALID_ARG,
+              "%s: null key_hist", fn);
+  return indexer_run(fn, q, q_dtype, weights, k_index_cache, k_dtype, num_pages,
+                     real_page_table, rpt_stride, token_to_req, seqlens_expanded,
+                     T, Hi, Di, page_size, max_seqlen_k, logits, logits_stride,
+                     key_hist, stream);
 }

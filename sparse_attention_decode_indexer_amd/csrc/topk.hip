@@ -27,15 +27,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 2048;
-
-// Order-preserving image of a float in uint32: NaN ranks lowest and -0.0
-// equals +0.0 (so equal values tie and are broken by position).
-__device__ __forceinline__ uint32_t order_key(float x) {
-  if (x != x) return 0u;
-  const uint32_t u = x == 0.0f ? 0u : __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Calls f(i, key) for every i in [0, n), 4 consecutive elements per thread
 // per iteration (float4 loads when the row is 16-byte aligned).
@@ -287,12 +278,16 @@ topk_hist_kernel(const float* __restrict__ logits, int64_t logits_stride,
 // positions (a radix select on position). The chosen candidates are marked
 // too, and a block-wide scan of the bitmap writes the kept positions in
 // ascending order (through the page table when given).
-template <bool VEC>
+// GIVEN: the row histograms come from the indexer (key_hist, [T][4096]
+// uint32) instead of pass 1; each row of key_hist is cleared once read, and a
+// row whose counts do not add up to its length takes the multi-pass select.
+template <bool VEC, bool GIVEN>
 __global__ void __launch_bounds__(kThreads)
 topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
                    const int32_t* __restrict__ lengths, int topk,
                    int max_seqlen_k, int chunks,
                    const uint16_t* __restrict__ ws,
+                   uint32_t* __restrict__ key_hist,
                    const int32_t* __restrict__ table, int64_t table_stride,
                    const int32_t* __restrict__ t2r, int32_t* __restrict__ out,
                    int64_t out_stride) {
@@ -313,25 +308,44 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   auto map = [&](int i) -> int32_t {
     return trow ? (trow[i >> 6] << 6) + (i & 63) : i;
   };
+  static_assert(kThreads * 4 == kHistBins && kHistBins == kKeyBins, "one thread per 4 bins");
+  uint4* hrow4 = GIVEN ? reinterpret_cast<uint4*>(key_hist + t * kHistBins) : nullptr;
   if (n <= topk) {
     for (int j = tid; j < topk; j += kThreads) orow[j] = j < n ? map(j) : -1;
+    if (GIVEN) hrow4[tid] = make_uint4(0, 0, 0, 0);
     return;
   }
   const float* row = logits + t * logits_stride;
 
   // ---- row histogram of the top 12 key bits and its threshold bin: each
-  // thread sums 4 bins of every chunk with 8-byte loads
-  const int nch = (n + kChunk - 1) / kChunk;
-  const uint16_t* hrow = ws + t * chunks * kHistBins;
+  // thread owns 4 bins (given, then cleared; or summed over the chunks of
+  // pass 1 with 8-byte loads)
+  uint32_t hs = 0;   // this thread's count
   {
-    static_assert(kThreads * 4 == kHistBins, "one thread per 4 bins");
     const int b4 = tid * 4;
     uint32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-    for (int c = 0; c < nch; ++c) {
-      const uint2 v = *reinterpret_cast<const uint2*>(hrow + c * kHistBins + b4);
-      s0 += v.x & 0xFFFFu; s1 += v.x >> 16; s2 += v.y & 0xFFFFu; s3 += v.y >> 16;
+    if constexpr (GIVEN) {
+      const uint4 v = hrow4[tid];
+      hrow4[tid] = make_uint4(0, 0, 0, 0);
+      s0 = v.x; s1 = v.y; s2 = v.z; s3 = v.w;
+    } else {
+      const int nch = (n + kChunk - 1) / kChunk;
+      const uint16_t* hrow = ws + t * chunks * kHistBins;
+      for (int c = 0; c < nch; ++c) {
+        const uint2 v = *reinterpret_cast<const uint2*>(hrow + c * kHistBins + b4);
+        s0 += v.x & 0xFFFFu; s1 += v.x >> 16; s2 += v.y & 0xFFFFu; s3 += v.y >> 16;
+      }
     }
     *reinterpret_cast<uint4*>(&hist[b4]) = make_uint4(s0, s1, s2, s3);
+    hs = s0 + s1 + s2 + s3;
+  }
+  if constexpr (GIVEN) {
+    int tot;
+    block_exclusive_scan((int)hs, scan_buf, &tot);
+    if (tot != n) {   // not the histogram of these logits
+      select_multipass(row, n, VEC, topk, orow, map, hist, scan_buf, s_sel);
+      return;
+    }
   }
   const int nw = (n + 31) >> 5;
   if (n <= kMapBits)
@@ -554,9 +568,47 @@ extern "C" int nsa_topk_transform(const float* logits, int64_t logits_stride,
     int st = nsa::check_launch(fn);
     if (st != NSA_OK) return st;
   }
-  auto sel = vec ? topk_select_kernel<true> : topk_select_kernel<false>;
+  auto sel = vec ? topk_select_kernel<true, false> : topk_select_kernel<false, false>;
   hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, s, logits, logits_stride,
-                     lengths, topk, max_seqlen_k, chunks, ws, table,
+                     lengths, topk, max_seqlen_k, chunks, ws, nullptr, table,
                      table_stride, token_to_req, out, out_stride);
+  return nsa::check_launch(fn);
+}
+
+extern "C" int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
+                                       const int32_t* lengths, int T, int topk,
+                                       int max_seqlen_k, const int32_t* table,
+                                       int64_t table_stride,
+                                       const int32_t* token_to_req, int page_size,
+                                       uint32_t* key_hist, int32_t* out,
+                                       int64_t out_stride, void* stream) {
+  const char* fn = "nsa_topk_transform_hist";
+  NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG,
+              "%s: negative size", fn);
+  NSA_REQUIRE(topk > 0, NSA_ERR_INVALID_ARG, "%s: topk must be positive", fn);
+  NSA_REQUIRE(page_size == NSA_PAGE_SIZE, NSA_ERR_UNSUPPORTED,
+              "%s: page_size %d (only 64 is supported)", fn, page_size);
+  if (T == 0) return nsa::ok();
+  NSA_REQUIRE(lengths && out && key_hist, NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  NSA_REQUIRE(nsa::aligned(key_hist, 16), NSA_ERR_INVALID_ARG,
+              "%s: key_hist must be 16-byte aligned", fn);
+  NSA_REQUIRE(max_seqlen_k <= topk || logits != nullptr, NSA_ERR_INVALID_ARG,
+              "%s: null logits", fn);
+  NSA_REQUIRE(logits == nullptr || logits_stride >= max_seqlen_k,
+              NSA_ERR_INVALID_ARG, "%s: logits_stride < max_seqlen_k", fn);
+  NSA_REQUIRE(out_stride >= topk, NSA_ERR_INVALID_ARG, "%s: out_stride < topk",
+              fn);
+  if (table != nullptr) {
+    NSA_REQUIRE(token_to_req != nullptr, NSA_ERR_INVALID_ARG,
+                "%s: a table needs token_to_req", fn);
+    NSA_REQUIRE(table_stride >= (max_seqlen_k + 63) / 64, NSA_ERR_INVALID_ARG,
+                "%s: table_stride < ceil(max_seqlen_k/64)", fn);
+  }
+  const bool vec = logits && nsa::aligned(logits, 16) && logits_stride % 4 == 0;
+  auto sel = vec ? topk_select_kernel<true, true> : topk_select_kernel<false, true>;
+  hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, (hipStream_t)stream,
+                     logits, logits_stride, lengths, topk, max_seqlen_k, 0,
+                     nullptr, key_hist, table, table_stride, token_to_req, out,
+                     out_stride);
   return nsa::check_launch(fn);
 }

@@ -16,14 +16,17 @@ from helpers import (DEV, need_gpu, note, to_dev, oracle_metadata, gpu_metadata,
 pytestmark = pytest.mark.gpu
 
 
-def run_path(nsa, w, fused=True):
+def run_path(nsa, w, fused=True, hist=False):
     md = gpu_metadata(nsa, w)
+    kh = nsa.new_key_hist(w.num_rows, DEV) if hist else None
     logits = nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
                                     md["real_page_table"], md["token_to_req"],
                                     md["seqlens_expanded"], w.max_seqlen_k,
-                                    dtype=idx_dtype(nsa, w))
+                                    dtype=idx_dtype(nsa, w), key_hist=kh)
     logical = nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
-                                     w.max_seqlen_k)
+                                     w.max_seqlen_k, key_hist=kh)
+    if hist:
+        assert int(kh.abs().sum()) == 0, "the top-k clears the histogram it used"
     if fused:
         slots = nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                        w.max_seqlen_k, table=md["real_page_table"],
@@ -84,14 +87,16 @@ def check_rows(w, md, logits, logical, slots, cache, out, lse, rows):
     dict(name="verify", bs=2, seqlen_range=(100, 3000)),
     dict(name="extend", bs=2, extend_lens=[30, 70], prefix_lens=[100, 2500]),
 ])
-@pytest.mark.parametrize("fused", [True, False])
-def test_pipeline_small(case, fused):
+@pytest.mark.parametrize("fused,hist", [(True, False), (False, False), (True, True)])
+def test_pipeline_small(case, fused, hist):
     nsa = need_gpu()
     case = dict(case)
     name = case.pop("name")
-    note(f"pipeline {name} {case} fused={fused}")
+    if hist and name == "tiny":
+        pytest.skip("the fused histogram is an fp8-indexer feature")
+    note(f"pipeline {name} {case} fused={fused} hist={hist}")
     w = to_dev(W.make_workload(name, **case))
-    res = run_path(nsa, w, fused=fused)
+    res = run_path(nsa, w, fused=fused, hist=hist)
     check_rows(w, *res, rows=list(range(w.num_rows)))
 
 
@@ -104,3 +109,48 @@ def test_pipeline_full_size_sampled(name):
     L = oracle_metadata(w)["seqlens_expanded"]
     rows = sorted({0, int(np.argmax(L)), int(np.argmin(L)), w.num_rows - 1})
     check_rows(w, *res, rows=rows)
+
+
+def _host_key_hist(logits_row, n):
+    """Histogram of the top 12 bits of the order-preserving key (NaN lowest,
+    -0 == +0) over positions [0, n): the definition stated in nsa.h."""
+    x = np.ascontiguousarray(logits_row[:n], dtype=np.float32)
+    u = x.view(np.uint32).copy()
+    u[x == 0] = 0
+    neg = (u & 0x80000000) != 0
+    key = np.where(neg, ~u, u | 0x80000000).astype(np.uint32)
+    key[np.isnan(x)] = 0
+    return np.bincount(key >> 20, minlength=4096)
+
+
+@pytest.mark.parametrize("name", ["decode_b32", "verify"])
+def test_fused_histogram_exact_and_topk_identical(name):
+    nsa = need_gpu()
+    w = full_workload(name)
+    note(f"fused histogram {name}: T={w.num_rows}")
+    md = gpu_metadata(nsa, w)
+    kh = nsa.new_key_hist(w.num_rows, DEV)
+    logits = nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
+                                    md["real_page_table"], md["token_to_req"],
+                                    md["seqlens_expanded"], w.max_seqlen_k,
+                                    dtype=idx_dtype(nsa, w), key_hist=kh)
+    torch.cuda.synchronize()
+    L = md["seqlens_expanded"].cpu().numpy()
+    hist = kh.cpu().numpy().view(np.uint32)
+    for t in sorted({0, int(np.argmax(L)), int(np.argmin(L)), w.num_rows - 1}):
+        n = min(int(L[t]), w.max_seqlen_k)
+        np.testing.assert_array_equal(hist[t], _host_key_hist(logits[t].cpu().numpy(), n),
+                                      err_msg=f"{name} row {t}")
+    assert (hist.sum(axis=1) == np.minimum(L, w.max_seqlen_k)).all()
+    args = (logits, md["seqlens_expanded"], w.topk, w.max_seqlen_k)
+    kw = dict(table=md["real_page_table"], token_to_req=md["token_to_req"])
+    plain = nsa.nsa_topk_transform(*args, **kw)
+    fused = nsa.nsa_topk_transform(*args, key_hist=kh, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, fused)
+    assert int(kh.abs().sum()) == 0
+    # a histogram that does not match the logits (here: all zero) takes the
+    # exact multi-pass path and still gives the same selection
+    again = nsa.nsa_topk_transform(*args, key_hist=kh, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, again)
