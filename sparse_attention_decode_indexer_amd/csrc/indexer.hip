@@ -9,7 +9,13 @@
 //   logits[t, s] = kscale[s] * sum_h w[t, h] * relu(q[t, h, :] . k[s, :]).
 //
 // fp8 path (Hi = 64 heads, Di = 128), MI355X design:
-//   * one block of 4 waves per (row, chunk of 32 pages); wave w takes pages
+//   * one block of 4 waves per (row, chunk of 32 pages), in plain row-major
+//     order with the chunk count per row padded to an odd number: work groups
+//     are dealt to the 8 XCDs round-robin, so a row's chunks start on a
+//     different XCD than the previous row's and rows of unequal length
+//     spread evenly (an even count pins chunk c to XCD c mod 8, and the
+//     XCDs holding the low chunks, which every row has, finish last);
+//   * wave w takes pages
 //     w, w+4, ... of the chunk, so a wave always works on a whole page
 //     (64 tokens = 8 KB of keys + 256 B of scales, contiguous); two page
 //     buffers per wave keep the register count at 140 (three waves per
@@ -38,13 +44,6 @@ constexpr int kDim = 128;
 constexpr int kPageBytesFp8 = kPage * kDim + kPage * 4;  // 8448
 constexpr int kWaves = 4;
 constexpr int kPagesPerBlock = 32;
-
-// Logical block id such that consecutive ids run on the same XCD (work
-// groups are dealt to the 8 XCDs round-robin).
-__device__ __forceinline__ uint32_t xcd_logical_block(uint32_t bid, uint32_t n) {
-  const uint32_t q = n / 8, r = n % 8, x = bid % 8;
-  return x * q + (x < r ? x : r) + bid / 8;
-}
 
 struct PageKeys {
   i32x8 k[4];  // 4 tiles of 16 tokens
@@ -80,9 +79,8 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    float* __restrict__ logits, int64_t logits_stride,
                    int chunks_per_row, uint32_t* __restrict__ key_hist) {
   __shared__ uint32_t lhist[HIST ? kKeyBins : 1];
-  const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int64_t t = lb / chunks_per_row;
-  const int chunk = lb % chunks_per_row;
+  const int64_t t = blockIdx.x / chunks_per_row;
+  const int chunk = blockIdx.x % chunks_per_row;
   int L = seqlens[t];
   L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
   const int npages = (L + kPage - 1) / kPage;
@@ -274,7 +272,8 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
               NSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   hipStream_t s = (hipStream_t)stream;
   if (fp8) {
-    const int chunks = (int)((ncols + kPagesPerBlock - 1) / kPagesPerBlock);
+    // odd, so that consecutive rows start on different XCDs
+    const int chunks = (int)((ncols + kPagesPerBlock - 1) / kPagesPerBlock) | 1;
     const int64_t blocks = (int64_t)T * chunks;
     NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
     auto kern = key_hist ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>;
