@@ -42,12 +42,39 @@ def _check(t, name, dtype=None, ndim=None, contiguous=True):
         raise ValueError(f"{name} must be contiguous")
 
 
+def new_metadata_buffers(mode, bs, num_q_rows, max_seqlen_k, device,
+                         want_page_table_1=False):
+    """Caller-owned metadata outputs for ``nsa_build_metadata(out=...)``:
+    static buffers that a captured graph keeps referring to while the inputs
+    (seq_lens, req_to_token, ...) are refreshed in place between replays."""
+    i32 = torch.int32
+    T = int(num_q_rows)
+    ncols = (max_seqlen_k + PAGE_SIZE - 1) // PAGE_SIZE
+    nq = bs + 1 if mode == MODE_EXTEND else T + 1
+    out = dict(
+        cache_seqlens=torch.empty(bs, dtype=i32, device=device),
+        cu_seqlens_k=torch.empty(bs + 1, dtype=i32, device=device),
+        cu_seqlens_q=torch.empty(nq, dtype=i32, device=device),
+        seqlens_expanded=torch.empty(T, dtype=i32, device=device),
+        nsa_cache_seqlens=torch.empty(T, dtype=i32, device=device),
+        nsa_cu_seqlens_k=torch.empty(T + 1, dtype=i32, device=device),
+        nsa_cu_seqlens_q=torch.empty(T + 1, dtype=i32, device=device),
+        real_page_table=torch.empty(bs, max(ncols, 1), dtype=i32, device=device),
+        token_to_req=torch.empty(T, dtype=i32, device=device),
+    )
+    if want_page_table_1:
+        out["page_table_1"] = torch.empty(bs, max(max_seqlen_k, 1), dtype=i32,
+                                          device=device)
+    return out
+
+
 def nsa_build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
                        max_seqlen_k, num_q_rows, extend_lens=None,
                        draft_token_num=0, page_size=PAGE_SIZE,
-                       want_page_table_1=False):
+                       want_page_table_1=False, out=None):
     """Per-forward metadata (one kernel launch). Returns a dict of int32
-    device tensors named as in nsa.h."""
+    device tensors named as in nsa.h: ``out`` (from new_metadata_buffers)
+    when given, else newly allocated ones."""
     i32 = torch.int32
     _check(seq_lens, "seq_lens", i32, 1)
     _check(req_to_token, "req_to_token", i32, 2)
@@ -57,21 +84,30 @@ def nsa_build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
     bs = seq_lens.numel()
     T = int(num_q_rows)
     dev = seq_lens.device
-    ncols = (max_seqlen_k + PAGE_SIZE - 1) // PAGE_SIZE
-    nq = bs + 1 if mode == MODE_EXTEND else T + 1
-    out = dict(
-        cache_seqlens=torch.empty(bs, dtype=i32, device=dev),
-        cu_seqlens_k=torch.empty(bs + 1, dtype=i32, device=dev),
-        cu_seqlens_q=torch.empty(nq, dtype=i32, device=dev),
-        seqlens_expanded=torch.empty(T, dtype=i32, device=dev),
-        nsa_cache_seqlens=torch.empty(T, dtype=i32, device=dev),
-        nsa_cu_seqlens_k=torch.empty(T + 1, dtype=i32, device=dev),
-        nsa_cu_seqlens_q=torch.empty(T + 1, dtype=i32, device=dev),
-        real_page_table=torch.empty(bs, max(ncols, 1), dtype=i32, device=dev),
-        token_to_req=torch.empty(T, dtype=i32, device=dev),
-    )
-    pt1 = (torch.empty(bs, max(max_seqlen_k, 1), dtype=i32, device=dev)
-           if want_page_table_1 else None)
+    if out is None:
+        out = new_metadata_buffers(mode, bs, T, max_seqlen_k, dev,
+                                   want_page_table_1)
+    else:
+        ncols = (max_seqlen_k + PAGE_SIZE - 1) // PAGE_SIZE
+        nq = bs + 1 if mode == MODE_EXTEND else T + 1
+        sizes = dict(cache_seqlens=bs, cu_seqlens_k=bs + 1, cu_seqlens_q=nq,
+                     seqlens_expanded=T, nsa_cache_seqlens=T,
+                     nsa_cu_seqlens_k=T + 1, nsa_cu_seqlens_q=T + 1,
+                     token_to_req=T)
+        for k, n in sizes.items():
+            _check(out[k], k, i32, 1)
+            if out[k].numel() < n:
+                raise ValueError(f"out[{k!r}] needs at least {n} entries")
+        tables = dict(real_page_table=max(ncols, 1))
+        if want_page_table_1:
+            if "page_table_1" not in out:
+                raise ValueError("out has no 'page_table_1'")
+            tables["page_table_1"] = max(max_seqlen_k, 1)
+        for k, cols in tables.items():
+            _check(out[k], k, i32, 2)
+            if out[k].shape[0] < bs or out[k].shape[1] < cols:
+                raise ValueError(f"out[{k!r}] must be at least [{bs}, {cols}]")
+    pt1 = out.get("page_table_1") if want_page_table_1 else None
     call("nsa_build_metadata", mode, bs, draft_token_num, topk, page_size,
          _ptr(seq_lens), _ptr(extend_lens), _ptr(req_to_token),
          req_to_token.stride(0), _ptr(req_pool_indices), max_seqlen_k, T,
@@ -81,8 +117,6 @@ def nsa_build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
          _ptr(out["nsa_cu_seqlens_q"]), _ptr(out["real_page_table"]),
          out["real_page_table"].stride(0), _ptr(out["token_to_req"]),
          _ptr(pt1), pt1.stride(0) if pt1 is not None else 0, _stream())
-    if pt1 is not None:
-        out["page_table_1"] = pt1
     return out
 
 
