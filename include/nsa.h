@@ -47,6 +47,8 @@ extern "C" {
 #define NSA_MODE_DECODE 0
 #define NSA_MODE_EXTEND 1
 #define NSA_MODE_TARGET_VERIFY 2
+#define NSA_MODE_DRAFT_EXTEND 3     /* draft model, per-request accepted + 1 */
+#define NSA_MODE_DRAFT_EXTEND_V2 4  /* draft model, draft_token_num each */
 
 #define NSA_DTYPE_FP32 0
 #define NSA_DTYPE_BF16 1
@@ -72,30 +74,38 @@ int nsa_version(void);
  * _transform_table_1_to_real and NativeSparseAttnBackend.init_forward_metadata;
  * [dsa-main] DeepseekSparseAttnBackend.init_forward_metadata (decode,
  * target-verify and extend branches) and _cal_indexer_k_start_end (per-token
- * batch index); [nsa-diff] target-verify metadata.
+ * batch index); [nsa-diff] target-verify metadata; [dsa-main]
+ * init_forward_metadata draft-extend branch and the draft-extend-v2 branch of
+ * init_forward_metadata_replay_cuda_graph (draft-extend rows are per token,
+ * as in target-verify, and seq_lens already count the new tokens).
  *
  * Inputs (device, int32):
- *   seq_lens[bs]          KV length per request (extend: including the new
- *                         tokens; target-verify: excluding the drafts).
- *   extend_lens[bs]       new tokens per request (EXTEND only, else NULL).
+ *   seq_lens[bs]          KV length per request (extend, draft-extend:
+ *                         including the new tokens; target-verify: excluding
+ *                         the drafts).
+ *   extend_lens[bs]       new tokens per request (EXTEND and DRAFT_EXTEND,
+ *                         else ignored / NULL).
  *   req_to_token          [pool_rows, rtt_stride] token -> physical slot.
  *   req_pool_indices[bs]  each request's row of req_to_token.
  * Host scalars:
  *   mode                  NSA_MODE_*.
- *   draft_token_num       draft tokens per request (TARGET_VERIFY, else 0).
+ *   draft_token_num       tokens per request of TARGET_VERIFY and
+ *                         DRAFT_EXTEND_V2 (>= 1), else ignored.
  *   topk                  selection size (clip for nsa_cache_seqlens).
  *   page_size             must be 64.
  *   max_seqlen_k          host bound >= every cache seqlen; sizes the tables.
- *   num_q_rows            T: bs (decode), bs*draft (verify), sum of
- *                         extend_lens (extend). Rows past T are never written.
+ *   num_q_rows            T: bs (decode), bs*draft (verify, draft-extend
+ *                         v2), sum of extend_lens (extend, draft-extend).
+ *                         Rows past T are never written.
  * Outputs (device, int32, caller-allocated):
  *   cache_seqlens[bs]         seq_lens (+ draft_token_num in verify).
  *   cu_seqlens_k[bs+1]        [0, cumsum(cache_seqlens)].
- *   cu_seqlens_q              decode and verify: [T+1] = arange(T+1) (every
- *                             verify draft token is its own query row);
+ *   cu_seqlens_q              decode, verify, draft-extend: [T+1] =
+ *                             arange(T+1) (every verify or draft-extend token
+ *                             is its own query row);
  *                             extend: [bs+1] = [0, cumsum(extend_lens)].
  *   seqlens_expanded[T]       visible KV length of each query row: decode =
- *                             cache_seqlens; verify/extend: kv_len - q_len + 1
+ *                             cache_seqlens; other modes: kv_len - q_len + 1
  *                             ... kv_len per request.
  *   nsa_cache_seqlens[T]      min(seqlens_expanded, topk).
  *   nsa_cu_seqlens_k[T+1]     [0, cumsum(nsa_cache_seqlens)].
@@ -298,6 +308,29 @@ int nsa_sparse_mla_extend(const void* q, int64_t q_tok_stride,
  */
 int nsa_quantize_k_cache(const void* kv_bf16, int64_t num_slots,
                          int64_t in_stride, void* out, void* stream);
+
+/* ---- f2: quantize-on-write of new latent rows --------------------------------------
+ * [dsa-main] forward_extend / forward_decode store each new token's latent
+ * row with token_to_kv_pool.set_mla_kv_buffer(layer, cache_loc, k, k_rope)
+ * before attention. This call writes row i into slot cache_loc[i] in the
+ * cache's own format: for NSA_KV_FP8_656 the 656-byte row is exactly what
+ * nsa_quantize_k_cache makes of the 576 values (so the fp8 cache never needs
+ * a whole-cache re-quantization), for NSA_KV_BF16_576 the values are copied.
+ *   k_nope      [n, nope_stride] bf16, first 512 elements used; 16-byte
+ *               aligned, nope_stride >= 512 and a multiple of 8.
+ *   k_rope      [n, rope_stride] bf16, first 64 elements used; bf16 cache:
+ *               16-byte aligned, rope_stride a multiple of 8.
+ *   cache_loc   [n] int32 destination slots; entries outside
+ *               [0, num_slots) are skipped. Entries must be distinct (two
+ *               rows to one slot race).
+ *   kv_cache    [num_slots, 656] bytes or [num_slots, 576] bf16, updated in
+ *               place; other slots are not touched.
+ * Nothing is allocated; n == 0 is a no-op.
+ */
+int nsa_set_mla_kv_buffer(const void* k_nope, int64_t nope_stride,
+                          const void* k_rope, int64_t rope_stride,
+                          const int32_t* cache_loc, int n, void* kv_cache,
+                          int kv_dtype, int64_t num_slots, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,11 @@ Follows the metadata construction on the pages:
   init_forward_metadata`` (decode, target-verify and extend branches) and
   ``_cal_indexer_k_start_end`` (the per-token batch index).
 * "nsa_backend.py (sglang 0.5.3rc2 -> 0.5.4 diff)", target-verify metadata.
+* Draft-extend (the speculative draft model's forward): "dsa_backend.py
+  (sglang main)", ``init_forward_metadata``, the draft-extend branch (v1:
+  each request extends by its own accepted count + 1; v2: every request by
+  the fixed number of draft tokens, ``seq_lens`` already counting them), and
+  the v2 branch of ``init_forward_metadata_replay_cuda_graph``.
 
 Readings where the pages are silent (each listed in the design doc):
 
@@ -17,6 +22,13 @@ Readings where the pages are silent (each listed in the design doc):
   the expanded seqlens "clipped to topk", read as an elementwise minimum.
 * Target-verify rows: one query row per draft token (``cu_seqlens_q`` steps by
   one, ``max_seqlen_q`` is 1), as the sglang-main page builds it.
+* Draft-extend rows: as on the sglang-main page, one query row per token
+  (``cu_seqlens_q`` steps by one, ``max_seqlen_q`` is 1) and the cache
+  lengths are ``seq_lens`` themselves (the 0.5.4 diff instead adds the draft
+  count to ``seq_lens`` and steps ``cu_seqlens_q`` per request).
+* ``seqlens_expand_triton`` is not shown; read as the per-request expansion
+  the 0.5.4 diff writes out for draft-extend: a request with q_len rows and
+  kv_len cached tokens gives rows kv_len - q_len + 1 .. kv_len.
 * ``real_page_table`` keeps one row per request; query rows reach it through
   ``token_to_req`` (the pages repeat the row once per draft token instead; the
   values seen by every query row are the same).
@@ -27,6 +39,8 @@ import numpy as np
 MODE_DECODE = 0
 MODE_EXTEND = 1
 MODE_TARGET_VERIFY = 2
+MODE_DRAFT_EXTEND = 3
+MODE_DRAFT_EXTEND_V2 = 4
 
 
 def compute_cu_seqlens(seqlens):
@@ -51,9 +65,11 @@ def build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
     """All metadata tensors of one forward pass, as int64 numpy arrays.
 
     Arguments follow the pages' ForwardBatch fields: ``seq_lens`` are the
-    per-request KV lengths (for extend: including the extend tokens; for
-    target-verify: excluding the draft tokens), ``extend_lens`` the
-    per-request number of new tokens (extend only), ``req_to_token`` the
+    per-request KV lengths (for extend and draft-extend: including the new
+    tokens; for target-verify: excluding the draft tokens), ``extend_lens``
+    the per-request number of new tokens (extend and draft-extend v1),
+    ``draft_token_num`` the fixed per-request count of target-verify and
+    draft-extend v2, ``req_to_token`` the
     ``[pool, max_ctx]`` token -> slot table and ``req_pool_indices`` each
     request's row in it. ``max_seqlen_k`` is the host-side bound that sizes the
     tables (default: the batch maximum of the cache seqlens, as the pages
@@ -100,6 +116,17 @@ def build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
                  for qo, kv in zip(ext, seq_lens)]
         seqlens_expanded = (np.concatenate(parts) if parts
                             else np.zeros(0, np.int64))
+    elif mode in (MODE_DRAFT_EXTEND, MODE_DRAFT_EXTEND_V2):
+        if mode == MODE_DRAFT_EXTEND:
+            q_lens = np.asarray(extend_lens, dtype=np.int64)
+        else:
+            q_lens = np.full(bs, draft_token_num, np.int64)
+        cu_seqlens_q = np.arange(int(q_lens.sum()) + 1, dtype=np.int64)
+        parts = [np.arange(kv - qo + 1, kv + 1, dtype=np.int64)
+                 for qo, kv in zip(q_lens, cache_seqlens)]
+        seqlens_expanded = (np.concatenate(parts) if parts
+                            else np.zeros(0, np.int64))
+        max_seqlen_q = 1
     else:
         raise ValueError(f"unsupported mode {mode}")
 

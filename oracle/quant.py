@@ -86,3 +86,21 @@ class Fp8Cache:
 
     def rows(self, slots):
         return dequantize_rows(self.raw[np.asarray(slots, np.int64)])
+
+
+def set_mla_kv_buffer(cache, k_nope_bits, k_rope_bits, cache_loc, fp8):
+    """Quantize-on-write of new latent rows ("dsa_backend.py (sglang main)",
+    ``forward_extend`` / ``forward_decode``: ``set_mla_kv_buffer(layer,
+    cache_loc, k, k_rope)``): row i (512 no-rope + 64 rope bf16 bit patterns)
+    is stored at slot ``cache_loc[i]`` in the cache's own format -- the
+    656-byte encoding of ``quantize_k_cache`` for an fp8 cache, the 576 bf16
+    values for a bf16 cache. Slots outside the cache are skipped. Returns a
+    new cache array (``[slots, 656]`` uint8 or ``[slots, 576]`` uint16)."""
+    out = np.array(cache, copy=True)
+    rows = np.concatenate([np.asarray(k_nope_bits, np.uint16)[:, :D_NOPE],
+                           np.asarray(k_rope_bits, np.uint16)[:, :D_ROPE]], axis=1)
+    for i, slot in enumerate(np.asarray(cache_loc, dtype=np.int64)):
+        if not 0 <= slot < out.shape[0]:
+            continue
+        out[slot] = quantize_k_cache(rows[i:i + 1])[0] if fp8 else rows[i]
+    return out

@@ -16,6 +16,7 @@ import torch
 from ._lib import NsaError, call, load  # noqa: F401
 
 MODE_DECODE, MODE_EXTEND, MODE_TARGET_VERIFY = 0, 1, 2
+MODE_DRAFT_EXTEND, MODE_DRAFT_EXTEND_V2 = 3, 4
 DTYPE_FP32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 KV_BF16_576, KV_FP8_656 = 0, 1
 PAGE_SIZE, D_QK, D_V = 64, 576, 512
@@ -292,3 +293,27 @@ def nsa_quantize_k_cache(kv_bf16, out=None):
     call("nsa_quantize_k_cache", _ptr(kv_bf16), n, kv_bf16.stride(0), _ptr(out),
          _stream())
     return out
+
+
+def nsa_set_mla_kv_buffer(k_nope, k_rope, cache_loc, kv_cache, kv_dtype):
+    """Write new latent rows into their cache slots, in place: row i of
+    k_nope [n, >=512] / k_rope [n, >=64] (bf16, rows contiguous) goes to slot
+    cache_loc[i] (int32; out-of-range entries skipped) of kv_cache
+    ([slots, 656] uint8 for KV_FP8_656, quantized as nsa_quantize_k_cache
+    does; [slots, 576] bf16 for KV_BF16_576). Returns kv_cache."""
+    for t, name in ((k_nope, "k_nope"), (k_rope, "k_rope")):
+        _check(t, name, torch.bfloat16, 2, contiguous=False)
+        if t.stride(1) != 1:
+            raise ValueError(f"{name} rows must be contiguous")
+    _check(cache_loc, "cache_loc", torch.int32, 1)
+    n = cache_loc.numel()
+    if k_nope.shape[0] < n or k_rope.shape[0] < n:
+        raise ValueError("k_nope / k_rope need a row per cache_loc entry")
+    if kv_dtype == KV_FP8_656:
+        _check(kv_cache, "kv_cache", torch.uint8, 2)
+    else:
+        _check(kv_cache, "kv_cache", torch.bfloat16, 2)
+    call("nsa_set_mla_kv_buffer", _ptr(k_nope), k_nope.stride(0), _ptr(k_rope),
+         k_rope.stride(0), _ptr(cache_loc), n, _ptr(kv_cache), kv_dtype,
+         kv_cache.shape[0], _stream())
+    return kv_cache

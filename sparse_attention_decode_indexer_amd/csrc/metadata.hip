@@ -4,7 +4,7 @@
 // fork)" (NSAMetadata, compute_cu_seqlens, _transform_table_1_to_real,
 // NativeSparseAttnBackend.init_forward_metadata) and "dsa_backend.py (sglang
 // main)" (DeepseekSparseAttnBackend.init_forward_metadata: decode,
-// target-verify and extend branches). The pages build these tensors with a
+// target-verify, draft-extend and extend branches). The pages build these tensors with a
 // chain of torch ops plus a host sync for max(seq_lens); here one kernel
 // writes all of them with the bound given by the host.
 //
@@ -32,8 +32,8 @@ __device__ __forceinline__ long long clipped_sum(long long a, long long n,
 __device__ __forceinline__ int q_rows_of(int mode, int draft,
                                          const int32_t* extend_lens, int i) {
   if (mode == NSA_MODE_DECODE) return 1;
-  if (mode == NSA_MODE_TARGET_VERIFY) return draft;
-  return extend_lens[i];
+  if (mode == NSA_MODE_TARGET_VERIFY || mode == NSA_MODE_DRAFT_EXTEND_V2) return draft;
+  return extend_lens[i];   // EXTEND, DRAFT_EXTEND
 }
 
 // Block-wide sums of three values: wave reductions with shuffles, then one
@@ -156,8 +156,7 @@ extern "C" int nsa_build_metadata(
     int32_t* real_page_table, int64_t rpt_stride, int32_t* token_to_req,
     int32_t* page_table_1, int64_t pt1_stride, void* stream) {
   const char* fn = "nsa_build_metadata";
-  NSA_REQUIRE(mode == NSA_MODE_DECODE || mode == NSA_MODE_EXTEND ||
-                  mode == NSA_MODE_TARGET_VERIFY,
+  NSA_REQUIRE(mode >= NSA_MODE_DECODE && mode <= NSA_MODE_DRAFT_EXTEND_V2,
               NSA_ERR_INVALID_ARG, "%s: unknown mode %d", fn, mode);
   NSA_REQUIRE(bs >= 0 && bs <= kMaxBatch, NSA_ERR_UNSUPPORTED,
               "%s: bs %d outside [0, %d]", fn, bs, kMaxBatch);
@@ -166,9 +165,9 @@ extern "C" int nsa_build_metadata(
               "%s: page_size %d (only 64 is supported)", fn, page_size);
   NSA_REQUIRE(max_seqlen_k >= 0 && num_q_rows >= 0, NSA_ERR_INVALID_ARG,
               "%s: negative max_seqlen_k or num_q_rows", fn);
-  if (mode == NSA_MODE_TARGET_VERIFY) {
+  if (mode == NSA_MODE_TARGET_VERIFY || mode == NSA_MODE_DRAFT_EXTEND_V2) {
     NSA_REQUIRE(draft_token_num >= 1, NSA_ERR_INVALID_ARG,
-                "%s: target-verify needs draft_token_num >= 1", fn);
+                "%s: mode %d needs draft_token_num >= 1", fn, mode);
     NSA_REQUIRE((int64_t)num_q_rows == (int64_t)bs * draft_token_num,
                 NSA_ERR_INVALID_ARG,
                 "%s: num_q_rows %d != bs * draft_token_num", fn, num_q_rows);
@@ -177,7 +176,7 @@ extern "C" int nsa_build_metadata(
                 "%s: decode needs num_q_rows == bs", fn);
   } else {
     NSA_REQUIRE(extend_lens != nullptr, NSA_ERR_INVALID_ARG,
-                "%s: extend needs extend_lens", fn);
+                "%s: extend and draft-extend need extend_lens", fn);
   }
   // buffers of zero length may be NULL (an empty batch has no rows)
   NSA_REQUIRE(cu_seqlens_k && cu_seqlens_q && nsa_cu_seqlens_k && nsa_cu_seqlens_q,

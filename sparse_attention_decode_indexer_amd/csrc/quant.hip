@@ -6,7 +6,14 @@
 // The byte layout and rounding (not on the pages) are the reading stated in
 // nsa.h: 512 codes in 4 blocks of 128, 4 fp32 scales amax/448, 64 bf16 rope.
 //
-// One wave per slot: lane l owns no-rope elements 8l..8l+7 (block l/16), so a
+// The same encoder also runs as quantize-on-write: "dsa_backend.py (sglang
+// main)", forward_extend / forward_decode, store the new tokens' latent rows
+// with token_to_kv_pool.set_mla_kv_buffer(layer, cache_loc, k, k_rope);
+// nsa_set_mla_kv_buffer writes row i to slot cache_loc[i], encoded in the
+// cache's own format (fp8 rows exactly as quantize_k_cache makes them, bf16
+// rows copied).
+//
+// One wave per row: lane l owns no-rope elements 8l..8l+7 (block l/16), so a
 // block's amax is a 16-lane reduction; lane l also copies rope element l.
 // The encoder is written from the e4m3fn definition (bias 7, 3 mantissa bits,
 // subnormals below 2^-6, largest finite 448) with round-to-nearest-even and
@@ -46,13 +53,38 @@ __device__ __forceinline__ uint32_t encode_e4m3(float y) {
   return sign | code;
 }
 
+// Latent rows i = 0..n-1: 512 no-rope bf16 at nope + i * nope_stride, 64
+// rope bf16 at rope + i * rope_stride (elements).
+struct Rows {
+  const uint16_t* nope;
+  int64_t nope_stride;
+  const uint16_t* rope;
+  int64_t rope_stride;
+};
+
+// Destination slot of row i: i itself (whole-cache conversion) or
+// cache_loc[i]; a slot outside [0, num_slots) is skipped.
+template <bool SCATTER>
+__device__ __forceinline__ int64_t dest_slot(const int32_t* cache_loc, int64_t i,
+                                             int64_t num_slots) {
+  if constexpr (SCATTER) {
+    const int64_t s = cache_loc[i];
+    return (s >= 0 && s < num_slots) ? s : -1;
+  } else {
+    return i;
+  }
+}
+
+template <bool SCATTER>
 __global__ void __launch_bounds__(kThreads)
-quantize_k_cache_kernel(const uint16_t* __restrict__ kv, int64_t num_slots,
-                        int64_t in_stride, uint8_t* __restrict__ out) {
+quantize_rows_kernel(Rows src, int64_t n, const int32_t* __restrict__ cache_loc,
+                     int64_t num_slots, uint8_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t slot = (int64_t)blockIdx.x * kSlotsPerBlock + (threadIdx.x >> 6);
-  if (slot >= num_slots) return;
-  const uint16_t* row = kv + slot * in_stride;
+  const int64_t i = (int64_t)blockIdx.x * kSlotsPerBlock + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const int64_t slot = dest_slot<SCATTER>(cache_loc, i, num_slots);
+  if (slot < 0) return;
+  const uint16_t* row = src.nope + i * src.nope_stride;
   uint8_t* orow = out + slot * 656;
 
   const uint4 raw = *reinterpret_cast<const uint4*>(row + lane * 8);
@@ -78,7 +110,25 @@ quantize_k_cache_kernel(const uint16_t* __restrict__ kv, int64_t num_slots,
   *reinterpret_cast<uint2*>(orow + lane * 8) = make_uint2(lo, hi);
   if ((lane & 15) == 0)
     *reinterpret_cast<float*>(orow + 512 + 4 * (lane >> 4)) = scale;
-  reinterpret_cast<uint16_t*>(orow + 528)[lane] = row[512 + lane];
+  reinterpret_cast<uint16_t*>(orow + 528)[lane] = src.rope[i * src.rope_stride + lane];
+}
+
+// bf16 cache rows: 512 + 64 values copied into the 1152-byte slot row (lane l
+// copies no-rope bytes 16l..16l+15; lanes 0..7 the rope bytes).
+__global__ void __launch_bounds__(kThreads)
+copy_rows_kernel(Rows src, int64_t n, const int32_t* __restrict__ cache_loc,
+                 int64_t num_slots, uint8_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * kSlotsPerBlock + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const int64_t slot = dest_slot<true>(cache_loc, i, num_slots);
+  if (slot < 0) return;
+  uint8_t* orow = out + slot * (NSA_D_QK * 2);
+  *reinterpret_cast<uint4*>(orow + 16 * lane) =
+      *reinterpret_cast<const uint4*>(src.nope + i * src.nope_stride + 8 * lane);
+  if (lane < 8)
+    *reinterpret_cast<uint4*>(orow + 1024 + 16 * lane) =
+        *reinterpret_cast<const uint4*>(src.rope + i * src.rope_stride + 8 * lane);
 }
 
 }  // namespace
@@ -96,9 +146,51 @@ extern "C" int nsa_quantize_k_cache(const void* kv_bf16, int64_t num_slots,
               NSA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
   const int64_t blocks = (num_slots + kSlotsPerBlock - 1) / kSlotsPerBlock;
   NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many slots", fn);
-  hipLaunchKernelGGL(quantize_k_cache_kernel, dim3((unsigned)blocks),
-                     dim3(kThreads), 0, (hipStream_t)stream,
-                     static_cast<const uint16_t*>(kv_bf16), num_slots,
-                     in_stride, static_cast<uint8_t*>(out));
+  const uint16_t* kv = static_cast<const uint16_t*>(kv_bf16);
+  const Rows src{kv, in_stride, kv + 512, in_stride};
+  hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3((unsigned)blocks),
+                     dim3(kThreads), 0, (hipStream_t)stream, src, num_slots,
+                     nullptr, num_slots, static_cast<uint8_t*>(out));
+  return nsa::check_launch(fn);
+}
+
+extern "C" int nsa_set_mla_kv_buffer(const void* k_nope, int64_t nope_stride,
+                                     const void* k_rope, int64_t rope_stride,
+                                     const int32_t* cache_loc, int n,
+                                     void* kv_cache, int kv_dtype,
+                                     int64_t num_slots, void* stream) {
+  const char* fn = "nsa_set_mla_kv_buffer";
+  NSA_REQUIRE(n >= 0 && num_slots >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(kv_dtype == NSA_KV_BF16_576 || kv_dtype == NSA_KV_FP8_656,
+              NSA_ERR_UNSUPPORTED, "%s: kv_dtype %d", fn, kv_dtype);
+  if (n == 0 || num_slots == 0) return nsa::ok();
+  NSA_REQUIRE(k_nope && k_rope && cache_loc && kv_cache, NSA_ERR_INVALID_ARG,
+              "%s: null pointer", fn);
+  NSA_REQUIRE(nope_stride >= NSA_D_V && nope_stride % 8 == 0 && nsa::aligned(k_nope, 16),
+              NSA_ERR_INVALID_ARG,
+              "%s: k_nope must be 16-byte aligned with a row stride >= 512 "
+              "and a multiple of 8", fn);
+  NSA_REQUIRE(rope_stride >= NSA_D_QK - NSA_D_V, NSA_ERR_INVALID_ARG,
+              "%s: rope_stride < 64", fn);
+  if (kv_dtype == NSA_KV_BF16_576)
+    NSA_REQUIRE(rope_stride % 8 == 0 && nsa::aligned(k_rope, 16), NSA_ERR_INVALID_ARG,
+                "%s: for a bf16 cache k_rope must be 16-byte aligned with a row "
+                "stride that is a multiple of 8", fn);
+  else
+    NSA_REQUIRE(nsa::aligned(k_rope, 2), NSA_ERR_INVALID_ARG,
+                "%s: k_rope must be 2-byte aligned", fn);
+  NSA_REQUIRE(nsa::aligned(kv_cache, 16), NSA_ERR_INVALID_ARG,
+              "%s: kv_cache must be 16-byte aligned", fn);
+  const int64_t blocks = ((int64_t)n + kSlotsPerBlock - 1) / kSlotsPerBlock;
+  const Rows src{static_cast<const uint16_t*>(k_nope), nope_stride,
+                 static_cast<const uint16_t*>(k_rope), rope_stride};
+  uint8_t* dst = static_cast<uint8_t*>(kv_cache);
+  if (kv_dtype == NSA_KV_FP8_656)
+    hipLaunchKernelGGL(quantize_rows_kernel<true>, dim3((unsigned)blocks),
+                       dim3(kThreads), 0, (hipStream_t)stream, src, (int64_t)n,
+                       cache_loc, num_slots, dst);
+  else
+    hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       (hipStream_t)stream, src, (int64_t)n, cache_loc, num_slots, dst);
   return nsa::check_launch(fn);
 }

@@ -134,6 +134,29 @@ def test_quantize_rejects_bad_arguments(lib):
     assert lib.nsa_quantize_k_cache(N, 0, 576, N, N) == 0
 
 
+def test_set_mla_kv_buffer_rejects_bad_arguments(lib):
+    p, loc = ctypes.c_void_p(256), ctypes.c_void_p(512)
+    ok = dict(k_nope=p, nope_stride=576, k_rope=ctypes.c_void_p(256 + 1024),
+              rope_stride=576, cache_loc=loc, n=4, kv_cache=p,
+              kv_dtype=1, num_slots=100, stream=N)
+    f = lib.nsa_set_mla_kv_buffer
+    call = lambda **kw: f(*{**ok, **kw}.values())
+    assert call(n=0) == 0 and call(num_slots=0) == 0                # no-ops
+    assert call(kv_dtype=7) == -2
+    assert call(n=-1) == -1
+    assert call(k_nope=N) == -1
+    assert call(nope_stride=500) == -1                                # < 512
+    assert call(nope_stride=580) == -1                                # not a multiple of 8
+    assert call(k_nope=ctypes.c_void_p(264)) == -1                   # 8-byte aligned
+    assert call(rope_stride=60) == -1
+    assert call(k_rope=ctypes.c_void_p(257)) == -1                   # odd address
+    # a bf16 cache copies rope with 16-byte moves
+    assert call(kv_dtype=0, k_rope=ctypes.c_void_p(258)) == -1
+    assert call(kv_dtype=0, rope_stride=580) == -1
+    assert call(kv_cache=ctypes.c_void_p(8)) == -1
+    assert "nsa_set_mla_kv_buffer" in lib.nsa_last_error().decode()
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import sparse_attention_decode_indexer_amd as nsa

@@ -26,7 +26,8 @@ def _compare(md, ref, wide=False):
         np.testing.assert_array_equal(got, want, err_msg=f)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_b32", "decode_b128", "extend", "verify"])
+@pytest.mark.parametrize("name", ["tiny", "decode_b32", "decode_b128", "extend", "verify",
+                                  "draft_extend", "draft_extend_v2"])
 def test_metadata_full_configs(name):
     nsa = need_gpu()
     note(f"metadata {name}")

@@ -86,6 +86,8 @@ def check_rows(w, md, logits, logical, slots, cache, out, lse, rows):
     dict(name="decode_b128", bs=2, seqlen_range=(2000, 9000)),
     dict(name="verify", bs=2, seqlen_range=(100, 3000)),
     dict(name="extend", bs=2, extend_lens=[30, 70], prefix_lens=[100, 2500]),
+    dict(name="draft_extend", bs=3, seqlen_range=(100, 3000)),
+    dict(name="draft_extend_v2", bs=2, seqlen_range=(100, 3000)),
 ])
 @pytest.mark.parametrize("fused,hist", [(True, False), (False, False), (True, True)])
 def test_pipeline_small(case, fused, hist):
@@ -100,7 +102,8 @@ def test_pipeline_small(case, fused, hist):
     check_rows(w, *res, rows=list(range(w.num_rows)))
 
 
-@pytest.mark.parametrize("name", ["decode_b32", "decode_b128", "verify", "extend"])
+@pytest.mark.parametrize("name", ["decode_b32", "decode_b128", "verify", "extend",
+                                  "draft_extend"])
 def test_pipeline_full_size_sampled(name):
     nsa = need_gpu()
     w = full_workload(name)

@@ -46,6 +46,45 @@ def test_quantize_strided_rows():
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("fp8", [True, False])
+def test_set_mla_kv_buffer_matches_oracle(fp8):
+    # quantize-on-write: k / k_rope are column slices of one [n, 576] tensor
+    # (strided rows); destinations are distinct, some out of range
+    nsa = need_gpu()
+    note(f"set_mla_kv_buffer fp8={fp8}")
+    n, slots = 300, 5000
+    x = _special_rows(n, seed=11)
+    g = torch.Generator().manual_seed(4)
+    loc = torch.randperm(slots, generator=g)[:n].to(torch.int32)
+    loc[[3, 100]] = -1
+    loc[7] = slots + 5
+    xd = x.to(DEV)
+    if fp8:
+        init = torch.randint(0, 256, (slots, 656), generator=g, dtype=torch.uint8)
+        kvd = nsa.KV_FP8_656
+    else:
+        init = torch.randn(slots, 576, generator=g).to(torch.bfloat16)
+        kvd = nsa.KV_BF16_576
+    cache = init.to(DEV)
+    nsa.nsa_set_mla_kv_buffer(xd[:, :512], xd[:, 512:], loc.to(DEV), cache, kvd)
+    got = cache.cpu()
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    init_np = init.numpy() if fp8 else init.view(torch.int16).numpy().view(np.uint16)
+    want = oracle.quant.set_mla_kv_buffer(init_np, bits[:, :512], bits[:, 512:],
+                                          loc.numpy(), fp8=fp8)
+    got_np = got.numpy() if fp8 else got.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got_np, want)
+    if fp8:   # the same bytes as converting the rows with nsa_quantize_k_cache
+        conv = nsa.nsa_quantize_k_cache(xd).cpu()
+        ok = (loc >= 0) & (loc < slots)
+        np.testing.assert_array_equal(got[loc[ok].long()].numpy(), conv[ok].numpy())
+    # n == 0 is a no-op
+    nsa.nsa_set_mla_kv_buffer(xd[:0, :512], xd[:0, 512:],
+                              torch.zeros(0, dtype=torch.int32, device=DEV), cache, kvd)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.cpu(), got)
+
+
 def test_quantize_full_cache_sampled():
     nsa = need_gpu()
     w = full_workload("decode_b128")

@@ -1,5 +1,6 @@
 """Pins for the metadata oracle: the pages' worked extend example, the field
-invariants the pages state, and causality properties of the three modes."""
+invariants the pages state, causality properties of each mode, and the
+draft-extend modes against the modes they reduce to."""
 
 import json
 import os
@@ -102,6 +103,64 @@ def test_target_verify_causality():
     np.testing.assert_array_equal(md["token_to_req"], np.repeat(np.arange(3), D))
     _check_field_invariants(md, 66)
     _check_tables(md, rtt, rpi)
+
+
+def test_draft_extend_hand_example():
+    # draft-extend v1 ("dsa_backend.py (sglang main)", init_forward_metadata,
+    # draft-extend branch): seq_lens count the new tokens; request 0 accepted
+    # 2 drafts (extends by 3), request 1 none (extends by 1); every token is
+    # its own query row and sees its prefix plus itself
+    seq_lens, ext = [10, 7], [3, 1]
+    rtt, rpi = _alloc(seq_lens)
+    md = M.build_metadata(M.MODE_DRAFT_EXTEND, seq_lens, rtt, rpi, topk=9,
+                          extend_lens=ext)
+    np.testing.assert_array_equal(md["cache_seqlens"], [10, 7])
+    np.testing.assert_array_equal(md["seqlens_expanded"], [8, 9, 10, 7])
+    np.testing.assert_array_equal(md["nsa_cache_seqlens"], [8, 9, 9, 7])
+    np.testing.assert_array_equal(md["cu_seqlens_q"], [0, 1, 2, 3, 4])
+    np.testing.assert_array_equal(md["token_to_req"], [0, 0, 0, 1])
+    assert md["max_seqlen_q"] == 1
+    _check_field_invariants(md, 9)
+    _check_tables(md, rtt, rpi)
+
+
+def test_draft_extend_v2_is_verify_with_drafts_in_seq_lens():
+    # v2 extends every request by the draft count with seq_lens already
+    # holding the drafts; target-verify adds them itself: same forward
+    seq_lens, D = [5, 130, 64, 1000], 4
+    rtt, rpi = _alloc([n + D for n in seq_lens])
+    ver = M.build_metadata(M.MODE_TARGET_VERIFY, seq_lens, rtt, rpi, topk=100,
+                           draft_token_num=D)
+    v2 = M.build_metadata(M.MODE_DRAFT_EXTEND_V2, [n + D for n in seq_lens], rtt,
+                          rpi, topk=100, draft_token_num=D)
+    for k in ver:
+        np.testing.assert_array_equal(np.asarray(v2[k]), np.asarray(ver[k]), err_msg=k)
+    _check_field_invariants(v2, 100)
+
+
+def test_draft_extend_v1_reduces_to_v2_and_to_extend():
+    seq_lens, D = [40, 300, 77], 3
+    rtt, rpi = _alloc(seq_lens)
+    v1 = M.build_metadata(M.MODE_DRAFT_EXTEND, seq_lens, rtt, rpi, topk=64,
+                          extend_lens=[D] * 3)
+    v2 = M.build_metadata(M.MODE_DRAFT_EXTEND_V2, seq_lens, rtt, rpi, topk=64,
+                          draft_token_num=D)
+    for k in v2:
+        np.testing.assert_array_equal(np.asarray(v1[k]), np.asarray(v2[k]), err_msg=k)
+    # with variable lengths, the rows are those of a chunked extend of the
+    # same tokens; only the query offsets differ (one row per token)
+    ext = [1, 3, 2]
+    d1 = M.build_metadata(M.MODE_DRAFT_EXTEND, seq_lens, rtt, rpi, topk=64,
+                          extend_lens=ext)
+    ex = M.build_metadata(M.MODE_EXTEND, seq_lens, rtt, rpi, topk=64,
+                          extend_lens=ext)
+    for k in ("cache_seqlens", "cu_seqlens_k", "seqlens_expanded",
+              "nsa_cache_seqlens", "nsa_cu_seqlens_k", "nsa_cu_seqlens_q",
+              "real_page_table", "token_to_req"):
+        np.testing.assert_array_equal(d1[k], ex[k], err_msg=k)
+    np.testing.assert_array_equal(d1["cu_seqlens_q"], np.arange(sum(ext) + 1))
+    np.testing.assert_array_equal(ex["cu_seqlens_q"], [0, 1, 4, 6])
+    _check_field_invariants(d1, 64)
 
 
 @pytest.mark.parametrize("prefix", [[0, 0], [7, 0], [100, 33]])

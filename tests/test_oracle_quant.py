@@ -72,3 +72,33 @@ def test_decode_values():
     assert y[0] == 2.0 and y[200] == -1.0 and y[512] == 1.0
     assert np.count_nonzero(y) == 3
     assert e4m3_decode(np.array([0xC0], np.uint8))[0] == -2.0
+
+
+def test_set_mla_kv_buffer_scatter():
+    # quantize-on-write: each new row lands in its slot in the cache's
+    # format; other slots and out-of-range destinations leave no trace
+    bits, x = _bf16_bits(6, seed=5, scale=2.0)
+    nope, rope = bits[:, :512], bits[:, 512:]
+    slots = 10
+    rng = np.random.default_rng(0)
+    cache8 = rng.integers(0, 256, (slots, 656), dtype=np.uint8)
+    loc = np.array([7, 2, -1, 9, 10, 0])          # -1 and 10: skipped
+    out8 = Q.set_mla_kv_buffer(cache8, nope, rope, loc, fp8=True)
+    want = Q.quantize_k_cache(bits)
+    for i, s in enumerate(loc):
+        if 0 <= s < slots:
+            np.testing.assert_array_equal(out8[s], want[i])
+    untouched = [s for s in range(slots) if s not in set(loc.tolist())]
+    np.testing.assert_array_equal(out8[untouched], cache8[untouched])
+    # decoding a written row stays within the e4m3 half-ulp of its values
+    y = Q.dequantize_rows(out8[[7]])[0]
+    err = np.abs(y[:512] - x[0, :512])
+    scale = np.repeat(out8[7, 512:528].copy().view("<f4").astype(np.float64), 128)
+    assert (err <= np.maximum(np.abs(x[0, :512]) * 2.0 ** -4, scale * 2.0 ** -10) + 1e-300).all()
+    np.testing.assert_array_equal(y[512:], x[0, 512:])
+    # bf16 cache: the 576 values copied
+    cache16 = rng.integers(0, 1 << 16, (slots, 576), dtype=np.uint16)
+    out16 = Q.set_mla_kv_buffer(cache16, nope, rope, loc, fp8=False)
+    np.testing.assert_array_equal(out16[7], bits[0])
+    np.testing.assert_array_equal(out16[0], bits[5])
+    np.testing.assert_array_equal(out16[untouched], cache16[untouched])

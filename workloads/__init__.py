@@ -22,6 +22,11 @@ sparse-attention backend pages; every value is synthetic and seed-fixed):
                   32768]; MLA 16 heads, bf16 KV; indexer as above.
 * ``verify``      speculative target-verify, batch 64, 4 draft tokens,
                   prefixes U{16384..131072}; MLA 128 heads, fp8 KV.
+* ``draft_extend`` / ``draft_extend_v2``  the draft model's extend after a
+                  verify of 4 draft tokens, batch 64, KV lengths (already
+                  counting the new tokens) U{16384..131072}: v1 extends each
+                  request by its accepted count + 1, drawn U{1..4}; v2 by
+                  all 4. MLA 128 heads, fp8 KV (the verify configuration).
 
 Pages of every request come from one seed-fixed random permutation of the
 page pool (random physical page order); ``req_to_token[row, s] = page(s // 64)
@@ -36,6 +41,8 @@ import torch
 MODE_DECODE = 0
 MODE_EXTEND = 1
 MODE_TARGET_VERIFY = 2
+MODE_DRAFT_EXTEND = 3
+MODE_DRAFT_EXTEND_V2 = 4
 
 PAGE = 64
 D_NOPE = 512
@@ -58,6 +65,13 @@ CONFIGS = {
     "verify": dict(mode=MODE_TARGET_VERIFY, bs=64, draft=4,
                    seqlen_range=(16384, 131072), topk=2048, idx_heads=64,
                    idx_dim=128, idx_kind="fp8", heads=128, kv="fp8"),
+    "draft_extend": dict(mode=MODE_DRAFT_EXTEND, bs=64, draft=4,
+                         seqlen_range=(16384, 131072), topk=2048, idx_heads=64,
+                         idx_dim=128, idx_kind="fp8", heads=128, kv="fp8"),
+    "draft_extend_v2": dict(mode=MODE_DRAFT_EXTEND_V2, bs=64, draft=4,
+                            seqlen_range=(16384, 131072), topk=2048,
+                            idx_heads=64, idx_dim=128, idx_kind="fp8",
+                            heads=128, kv="fp8"),
 }
 
 SM_SCALE = 1.0 / math.sqrt(192.0)
@@ -119,7 +133,9 @@ def make_workload(name, device="cpu", seed=0, parts=("indexer", "attention"),
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     mode, bs = cfg["mode"], cfg["bs"]
-    draft = cfg.get("draft", 0) if mode == MODE_TARGET_VERIFY else 0
+    # fixed per-request token count of target-verify and draft-extend v2
+    draft = (cfg.get("draft", 0)
+             if mode in (MODE_TARGET_VERIFY, MODE_DRAFT_EXTEND_V2) else 0)
 
     if mode == MODE_EXTEND:
         ext = torch.tensor(cfg["extend_lens"][:bs], dtype=torch.int64)
@@ -135,9 +151,14 @@ def make_workload(name, device="cpu", seed=0, parts=("indexer", "attention"),
             lo, hi = cfg["seqlen_range"]
             seq_lens = _randint(gen, lo, hi, bs, dev)
         extend_lens = None
-        num_rows = bs * (draft if mode == MODE_TARGET_VERIFY else 1)
+        num_rows = bs * (draft if draft else 1)
+        if mode == MODE_DRAFT_EXTEND:   # accepted drafts + 1 per request
+            extend_lens = _randint(gen, 1, cfg["draft"], bs, dev)
+            num_rows = int(extend_lens.sum())
 
-    kv_lens = (seq_lens + draft).cpu()                  # tokens held per request
+    # tokens held per request: target-verify adds the drafts to seq_lens,
+    # the other modes count them in seq_lens already
+    kv_lens = (seq_lens + (draft if mode == MODE_TARGET_VERIFY else 0)).cpu()
     pages_per_req = [(int(n) + PAGE - 1) // PAGE for n in kv_lens]
     spare = 3
     num_pages = sum(pages_per_req) + spare
