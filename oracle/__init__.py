@@ -27,7 +27,11 @@ Modules, one per step of the path:
 * ``topk``      -- length-masked top-k.
 * ``transform`` -- logical position -> physical KV slot.
 * ``sparse_mla``-- MLA attention over the selected slots.
-* ``quant``     -- fp8 block-scaled latent-KV cache encoder / decoder.
+* ``quant``     -- fp8 block-scaled latent-KV cache encoder / decoder, and
+  quantize-on-write of new rows.
+* ``ragged``    -- the RAGGED extend route: per-token key windows, shifted
+  top-k positions, the flattened token table, paged dequantization, CSR
+  index lists.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 except the indexer's scoring formula itself, which the pages never show; the
@@ -35,4 +39,4 @@ oracle's implementation of the adopted reading is pinned by closed forms, but
 the reading is not (see ``indexer``).
 """
 
-from . import formats, metadata, indexer, topk, transform, sparse_mla, quant  # noqa: F401
+from . import formats, metadata, indexer, topk, transform, sparse_mla, quant, ragged  # noqa: F401
