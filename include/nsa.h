@@ -332,6 +332,70 @@ int nsa_set_mla_kv_buffer(const void* k_nope, int64_t nope_stride,
                           const int32_t* cache_loc, int n, void* kv_cache,
                           int kv_dtype, int64_t num_slots, void* stream);
 
+/* ---- f3: the RAGGED extend route ---------------------------------------------------
+ * [dsa-main] scores each extend token against the concatenated keys of the
+ * batch and attends over a contiguous bf16 copy of the batch's latent rows
+ * (init_forward_metadata extend branch: page_table_1_flattened,
+ * topk_indices_offset; _cal_indexer_k_start_end: ks / ke; forward_extend
+ * RAGGED: the shifted top-k positions and dequantize_k_cache_paged). The
+ * route composes with the other calls: nsa_indexer_logits + nsa_topk_transform
+ * (no table) give each row's positions relative to its request, which are
+ * the positions inside [ks, ke) minus ks; nsa_ragged_index_transform shifts
+ * them into the concatenation; nsa_dequantize_k_cache_paged builds the bf16
+ * rows of the flattened table; nsa_sparse_mla_extend then reads those rows
+ * (NSA_KV_BF16_576) with the shifted positions as slot indices.
+ *
+ * nsa_ragged_extend_metadata, from the outputs of nsa_build_metadata:
+ *   cu_seqlens_k[bs+1], cache_seqlens[bs], seqlens_expanded[T],
+ *   token_to_req[T], real_page_table [bs, rpt_stride]  (device, int32);
+ *   max_seqlen_k   the host bound used for nsa_build_metadata.
+ *   ks[T], ke[T]   the row's window [ks, ke) in the concatenated keys:
+ *                  ks = cu_seqlens_k[req], ke = ks + seqlens_expanded.
+ *   topk_indices_offset[T]  (nullable) = ks.
+ *   page_table_1_flattened  (nullable) [flat_capacity]: entry
+ *                  cu_seqlens_k[r] + s = slot of token s of request r, for
+ *                  s < cache_seqlens[r]; positions >= flat_capacity are not
+ *                  written (size it with the host's sum of cache lengths).
+ */
+int nsa_ragged_extend_metadata(const int32_t* cu_seqlens_k,
+                               const int32_t* cache_seqlens, int bs,
+                               const int32_t* seqlens_expanded,
+                               const int32_t* token_to_req, int T,
+                               const int32_t* real_page_table,
+                               int64_t rpt_stride, int max_seqlen_k,
+                               int32_t* ks, int32_t* ke,
+                               int32_t* topk_indices_offset,
+                               int32_t* page_table_1_flattened,
+                               int64_t flat_capacity, void* stream);
+
+/* out[t, j] = topk_indices[t, j] + offset[t] where the index is not -1, else
+ * -1 (forward_extend, RAGGED). [T, topk] int32 with row strides; in place
+ * (out == topk_indices) is allowed. */
+int nsa_ragged_index_transform(const int32_t* topk_indices, int64_t in_stride,
+                               int T, int topk, const int32_t* offset,
+                               int32_t* out, int64_t out_stride, void* stream);
+
+/* dequantize_k_cache_paged: out[i] = bf16 latent row of slot slots[i] of an
+ * NSA_KV_FP8_656 cache: each no-rope value = fp32 product of its e4m3 code
+ * and block scale, rounded to bf16 (nearest even); the 64 rope values copied;
+ * a slot outside [0, num_slots) gives a zero row (a reading: the body is not
+ * on the pages). out: [n, out_stride] bf16, out_stride >= 576 and a multiple
+ * of 8, 16-byte aligned. */
+int nsa_dequantize_k_cache_paged(const void* kv_fp8, int64_t num_slots,
+                                 const int32_t* slots, int64_t n, void* out,
+                                 int64_t out_stride, void* stream);
+
+/* CSR lists of the entries != -1 of an index matrix [T, topk] (the aiter
+ * route's get_valid_kv_indices in [dsa-main]): kv_indptr[T+1] =
+ * [0, cumsum(valid count per row)], kv_indices = every row's valid entries
+ * in column order, rows in order; entries beyond `capacity` are dropped
+ * (kv_indptr still counts them). Three launches (count, scan, write). For
+ * rows written by nsa_topk_transform (valid first) kv_indptr equals
+ * nsa_cu_seqlens_k. */
+int nsa_valid_kv_indices(const int32_t* indices, int64_t idx_stride, int T,
+                         int topk, int32_t* kv_indptr, int32_t* kv_indices,
+                         int64_t capacity, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

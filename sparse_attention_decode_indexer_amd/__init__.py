@@ -317,3 +317,72 @@ def nsa_set_mla_kv_buffer(k_nope, k_rope, cache_loc, kv_cache, kv_dtype):
          k_rope.stride(0), _ptr(cache_loc), n, _ptr(kv_cache), kv_dtype,
          kv_cache.shape[0], _stream())
     return kv_cache
+
+
+# ---- RAGGED extend route ----------------------------------------------------
+
+def nsa_ragged_extend_metadata(md, max_seqlen_k, total_k, want_flat=True):
+    """RAGGED-route metadata of an extend batch from nsa_build_metadata's
+    outputs ``md``: ks / ke (each row's window in the concatenated keys),
+    topk_indices_offset (= ks) and, with ``want_flat``,
+    page_table_1_flattened [total_k] (every cached token's slot, request after
+    request). ``total_k`` is the host-known sum of the cache lengths (the
+    pages' seq_lens_sum); ``max_seqlen_k`` the bound given to
+    nsa_build_metadata."""
+    i32 = torch.int32
+    T = md["seqlens_expanded"].numel()
+    bs = md["cache_seqlens"].numel()
+    dev = md["seqlens_expanded"].device
+    out = dict(ks=torch.empty(T, dtype=i32, device=dev),
+               ke=torch.empty(T, dtype=i32, device=dev),
+               topk_indices_offset=torch.empty(T, dtype=i32, device=dev))
+    flat = torch.empty(max(int(total_k), 0), dtype=i32, device=dev) if want_flat else None
+    rpt = md["real_page_table"]
+    call("nsa_ragged_extend_metadata", _ptr(md["cu_seqlens_k"]),
+         _ptr(md["cache_seqlens"]), bs, _ptr(md["seqlens_expanded"]),
+         _ptr(md["token_to_req"]), T, _ptr(rpt), rpt.stride(0), max_seqlen_k,
+         _ptr(out["ks"]), _ptr(out["ke"]), _ptr(out["topk_indices_offset"]),
+         _ptr(flat) if flat is not None and flat.numel() else None,
+         flat.numel() if flat is not None else 0, _stream())
+    if flat is not None:
+        out["page_table_1_flattened"] = flat
+    return out
+
+
+def nsa_ragged_index_transform(topk_indices, offset, out=None):
+    """Shift valid top-k positions [T, topk] by offset[T] (-1 kept)."""
+    _check(topk_indices, "topk_indices", torch.int32, 2)
+    _check(offset, "offset", torch.int32, 1)
+    T, k = topk_indices.shape
+    if out is None:
+        out = torch.empty_like(topk_indices)
+    _check(out, "out", torch.int32, 2)
+    call("nsa_ragged_index_transform", _ptr(topk_indices), topk_indices.stride(0),
+         T, k, _ptr(offset), _ptr(out), out.stride(0), _stream())
+    return out
+
+
+def nsa_dequantize_k_cache_paged(kv_fp8, slots, out=None):
+    """bf16 latent rows [n, 576] of the fp8 cache rows ``slots`` [n]."""
+    _check(kv_fp8, "kv_fp8", torch.uint8, 2)
+    _check(slots, "slots", torch.int32, 1)
+    n = slots.numel()
+    if out is None:
+        out = torch.empty(n, 576, dtype=torch.bfloat16, device=slots.device)
+    _check(out, "out", torch.bfloat16, 2, contiguous=False)
+    call("nsa_dequantize_k_cache_paged", _ptr(kv_fp8), kv_fp8.shape[0], _ptr(slots),
+         n, _ptr(out), out.stride(0), _stream())
+    return out
+
+
+def nsa_valid_kv_indices(indices, capacity=None):
+    """CSR lists of the entries != -1 of ``indices`` [T, topk]: (kv_indptr
+    [T+1], kv_indices [capacity]); ``capacity`` defaults to T * topk."""
+    _check(indices, "indices", torch.int32, 2)
+    T, k = indices.shape
+    cap = T * k if capacity is None else int(capacity)
+    indptr = torch.empty(T + 1, dtype=torch.int32, device=indices.device)
+    flat = torch.empty(max(cap, 1), dtype=torch.int32, device=indices.device)
+    call("nsa_valid_kv_indices", _ptr(indices), indices.stride(0), T, k,
+         _ptr(indptr), _ptr(flat), cap, _stream())
+    return indptr, flat[:cap]

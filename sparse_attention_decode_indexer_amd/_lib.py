@@ -42,6 +42,11 @@ SIGNATURES = {
     "nsa_quantize_k_cache": (c_int, [P, c_i64, c_i64, P, P]),
     "nsa_set_mla_kv_buffer": (c_int, [P, c_i64, P, c_i64, P, c_int, P, c_int,
                                       c_i64, P]),
+    "nsa_ragged_extend_metadata": (c_int, [P, P, c_int, P, P, c_int, P, c_i64,
+                                           c_int, P, P, P, P, c_i64, P]),
+    "nsa_ragged_index_transform": (c_int, [P, c_i64, c_int, c_int, P, P, c_i64, P]),
+    "nsa_dequantize_k_cache_paged": (c_int, [P, c_i64, P, c_i64, P, c_i64, P]),
+    "nsa_valid_kv_indices": (c_int, [P, c_i64, c_int, c_int, P, P, c_i64, P]),
 }
 
 _lib = None

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libnsa.so")
 
 SOURCES = ["status.cpp", "metadata.hip", "transform.hip", "topk.hip",
-           "indexer.hip", "sparse_mla.hip", "quant.hip"]
+           "indexer.hip", "sparse_mla.hip", "quant.hip", "ragged.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -131,7 +131,66 @@ copy_rows_kernel(Rows src, int64_t n, const int32_t* __restrict__ cache_loc,
         *reinterpret_cast<const uint4*>(src.rope + i * src.rope_stride + 8 * lane);
 }
 
+// The RAGGED extend route's dequantize_k_cache_paged ("dsa_backend.py
+// (sglang main)", forward_extend): row i of the output is the bf16 latent row
+// of slot slots[i] -- each no-rope value the fp32 product of its e4m3 code and
+// its block scale, rounded to bf16 (nearest even), the rope values copied; a
+// slot outside the cache gives a zero row. One wave per row; lane l decodes
+// values 8l..8l+7 (block l / 16) and lanes 0..7 copy 16 rope bytes each.
+__global__ void __launch_bounds__(kThreads)
+dequantize_paged_kernel(const uint8_t* __restrict__ cache, int64_t num_slots,
+                        const int32_t* __restrict__ slots, int64_t n,
+                        uint16_t* __restrict__ out, int64_t out_stride) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * kSlotsPerBlock + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const int64_t slot = slots[i];
+  const bool ok = slot >= 0 && slot < num_slots;
+  const uint8_t* row = cache + (ok ? slot : 0) * 656;
+  uint16_t* orow = out + i * out_stride;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (ok) {
+    const uint2 codes = *reinterpret_cast<const uint2*>(row + 8 * lane);
+    const float scale = *reinterpret_cast<const float*>(row + 512 + 4 * (lane >> 4));
+    const uint32_t w[2] = {codes.x, codes.y};
+    uint32_t bf[4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+      bf[2 * k] = pack_bf16x2(lo[0] * scale, lo[1] * scale);
+      bf[2 * k + 1] = pack_bf16x2(hi[0] * scale, hi[1] * scale);
+    }
+    v = make_uint4(bf[0], bf[1], bf[2], bf[3]);
+  }
+  *reinterpret_cast<uint4*>(orow + 8 * lane) = v;
+  if (lane < 8)
+    *reinterpret_cast<uint4*>(orow + 512 + 8 * lane) =
+        ok ? *reinterpret_cast<const uint4*>(row + 528 + 16 * lane) : make_uint4(0, 0, 0, 0);
+}
+
 }  // namespace
+
+extern "C" int nsa_dequantize_k_cache_paged(const void* kv_fp8, int64_t num_slots,
+                                            const int32_t* slots, int64_t n,
+                                            void* out, int64_t out_stride,
+                                            void* stream) {
+  const char* fn = "nsa_dequantize_k_cache_paged";
+  NSA_REQUIRE(n >= 0 && num_slots >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n == 0) return nsa::ok();
+  NSA_REQUIRE(slots && out && (kv_fp8 || num_slots == 0), NSA_ERR_INVALID_ARG,
+              "%s: null pointer", fn);
+  NSA_REQUIRE(out_stride >= NSA_D_QK && out_stride % 8 == 0, NSA_ERR_INVALID_ARG,
+              "%s: out_stride must be >= 576 and a multiple of 8", fn);
+  NSA_REQUIRE(nsa::aligned(out, 16) && nsa::aligned(kv_fp8, 16), NSA_ERR_INVALID_ARG,
+              "%s: out and kv_fp8 must be 16-byte aligned", fn);
+  const int64_t blocks = (n + kSlotsPerBlock - 1) / kSlotsPerBlock;
+  NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  hipLaunchKernelGGL(dequantize_paged_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, static_cast<const uint8_t*>(kv_fp8),
+                     num_slots, slots, n, static_cast<uint16_t*>(out), out_stride);
+  return nsa::check_launch(fn);
+}
 
 extern "C" int nsa_quantize_k_cache(const void* kv_bf16, int64_t num_slots,
                                     int64_t in_stride, void* out,

@@ -177,3 +177,29 @@ def test_fused_histogram_entry_points_validate(lib):
     assert lib.nsa_topk_transform_hist(P(16), 256, P(16), 1, 64, 256, N, 0, N, 64,
                                        P(18), P(16), 64, N) == -1
     assert "aligned" in _err(lib)
+
+
+def test_ragged_entry_points_validate(lib):
+    p = ctypes.c_void_p(256)
+    # metadata: nothing to do for empty inputs; null per-row outputs refused
+    assert lib.nsa_ragged_extend_metadata(N, N, 0, N, N, 0, N, 0, 0, N, N, N, N, 0, N) == 0
+    assert lib.nsa_ragged_extend_metadata(p, p, 2, p, p, 5, p, 4, 100, N, p, N, N, 0, N) == -1
+    assert lib.nsa_ragged_extend_metadata(p, p, -1, p, p, 5, p, 4, 100, p, p, N, N, 0, N) == -1
+    # flattened table: row stride below ceil(max_seqlen_k / 64)
+    assert lib.nsa_ragged_extend_metadata(p, p, 2, p, p, 0, p, 1, 100, N, N, N, p, 10, N) == -1
+    # index transform
+    assert lib.nsa_ragged_index_transform(N, 0, 0, 8, N, N, 0, N) == 0
+    assert lib.nsa_ragged_index_transform(p, 4, 3, 8, p, p, 8, N) == -1      # stride < topk
+    assert lib.nsa_ragged_index_transform(p, 8, 3, 8, N, p, 8, N) == -1      # null offset
+    # paged dequantization
+    assert lib.nsa_dequantize_k_cache_paged(p, 10, p, 0, p, 576, N) == 0
+    assert lib.nsa_dequantize_k_cache_paged(p, 10, p, 4, p, 570, N) == -1   # stride < 576
+    assert lib.nsa_dequantize_k_cache_paged(p, 10, p, 4, p, 580, N) == -1   # not a multiple of 8
+    assert lib.nsa_dequantize_k_cache_paged(p, 10, p, 4, ctypes.c_void_p(8), 576, N) == -1
+    assert lib.nsa_dequantize_k_cache_paged(p, 10, N, 4, p, 576, N) == -1
+    # CSR lists
+    assert lib.nsa_valid_kv_indices(p, 8, 2, 8, N, p, 16, N) == -1           # null indptr
+    assert lib.nsa_valid_kv_indices(p, 4, 2, 8, p, p, 16, N) == -1           # stride < topk
+    assert lib.nsa_valid_kv_indices(p, 8, 2, 8, p, N, 16, N) == -1           # null kv_indices
+    assert lib.nsa_valid_kv_indices(p, 8, -2, 8, p, p, 16, N) == -1
+    assert "nsa_valid_kv_indices" in lib.nsa_last_error().decode()
