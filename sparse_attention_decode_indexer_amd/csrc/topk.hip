@@ -110,6 +110,34 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, int nb,
   }
 }
 
+// Block-wide form of the same search: thread tid owns bins NB*tid ..
+// NB*tid + NB - 1 with counts c[] in registers, and `above` counts the keys
+// in the bins of all higher threads (from a block scan). The one thread whose
+// bins hold the krem-th largest key publishes s_sel = {bin, krem - keys
+// above the bin, bin taken whole, keys in the bin}; callers ensure the total
+// is at least krem and synchronise before reading s_sel.
+template <int NB>
+__device__ __forceinline__ void publish_threshold(const uint32_t (&c)[NB], uint32_t above,
+                                                  int krem, uint32_t* s_sel) {
+  uint32_t own = 0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) own += c[i];
+  if (above < (uint32_t)krem && above + own >= (uint32_t)krem) {
+    uint32_t a = above;
+#pragma unroll
+    for (int i = NB - 1; i >= 0; --i) {
+      if (a + c[i] >= (uint32_t)krem) {
+        s_sel[0] = NB * threadIdx.x + i;
+        s_sel[1] = krem - a;
+        s_sel[2] = (a + c[i] == (uint32_t)krem) ? 1u : 0u;
+        s_sel[3] = c[i];
+        break;
+      }
+      a += c[i];
+    }
+  }
+}
+
 // Multi-pass radix select over the row in global memory: the general path,
 // used when the threshold bin of the first-pass histogram holds too many
 // candidates for LDS (heavy ties) or topk exceeds the fast path's lists.
@@ -296,7 +324,7 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   __shared__ uint32_t cand_key[kCap];
   __shared__ int32_t cand_pos[kCap];
   __shared__ int scan_buf[2 * kWaves + 1];
-  __shared__ uint32_t s_sel[3];
+  __shared__ uint32_t s_sel[4];
   __shared__ int s_ncand;
 
   const int64_t t = blockIdx.x;
@@ -318,46 +346,42 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   const float* row = logits + t * logits_stride;
 
   // ---- row histogram of the top 12 key bits and its threshold bin: each
-  // thread owns 4 bins (given, then cleared; or summed over the chunks of
-  // pass 1 with 8-byte loads)
-  uint32_t hs = 0;   // this thread's count
+  // thread owns 4 bins in registers (given, then cleared; or summed over the
+  // chunks of pass 1 with 8-byte loads); one block scan gives the total and,
+  // for every thread, the keys in higher bins
+  uint32_t hc[4] = {0, 0, 0, 0};
   {
     const int b4 = tid * 4;
-    uint32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
     if constexpr (GIVEN) {
       const uint4 v = hrow4[tid];
       hrow4[tid] = make_uint4(0, 0, 0, 0);
-      s0 = v.x; s1 = v.y; s2 = v.z; s3 = v.w;
+      hc[0] = v.x; hc[1] = v.y; hc[2] = v.z; hc[3] = v.w;
     } else {
       const int nch = (n + kChunk - 1) / kChunk;
       const uint16_t* hrow = ws + t * chunks * kHistBins;
       for (int c = 0; c < nch; ++c) {
         const uint2 v = *reinterpret_cast<const uint2*>(hrow + c * kHistBins + b4);
-        s0 += v.x & 0xFFFFu; s1 += v.x >> 16; s2 += v.y & 0xFFFFu; s3 += v.y >> 16;
+        hc[0] += v.x & 0xFFFFu; hc[1] += v.x >> 16; hc[2] += v.y & 0xFFFFu; hc[3] += v.y >> 16;
       }
     }
-    *reinterpret_cast<uint4*>(&hist[b4]) = make_uint4(s0, s1, s2, s3);
-    hs = s0 + s1 + s2 + s3;
   }
-  if constexpr (GIVEN) {
-    int tot;
-    block_exclusive_scan((int)hs, scan_buf, &tot);
-    if (tot != n) {   // not the histogram of these logits
-      select_multipass(row, n, VEC, topk, orow, map, hist, scan_buf, s_sel);
-      return;
-    }
+  const uint32_t hs = hc[0] + hc[1] + hc[2] + hc[3];
+  int tot;
+  const int hex = block_exclusive_scan((int)hs, scan_buf, &tot);
+  if (tot != n) {   // not the histogram of these logits
+    select_multipass(row, n, VEC, topk, orow, map, hist, scan_buf, s_sel);
+    return;
   }
   const int nw = (n + 31) >> 5;
   if (n <= kMapBits)
     for (int w = tid; w < nw; w += kThreads) bitmap[w] = 0u;
   if (tid == 0) s_ncand = 0;
-  __syncthreads();
-  find_threshold_bin(hist, kHistBins, topk, s_sel);
+  publish_threshold<4>(hc, (uint32_t)(tot - hex) - hs, topk, s_sel);
   __syncthreads();
   const uint32_t bin = s_sel[0];
   int krem = (int)s_sel[1];
   bool exact = s_sel[2] != 0;
-  const uint32_t cnt_b = hist[bin];
+  const uint32_t cnt_b = s_sel[3];
   __syncthreads();
   if (cnt_b > (uint32_t)kCap || n > kMapBits) {
     select_multipass(row, n, VEC, topk, orow, map, hist, scan_buf, s_sel);
@@ -438,6 +462,17 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   }
   __syncthreads();
   const int nc = min(s_ncand, kCap);
+  // the row's page-table entries for the output, loaded now (branch-free:
+  // without a table the loads read lengths[0]) and put in LDS once the
+  // candidates are no longer needed
+  constexpr int kTabPer = kMapBits / NSA_PAGE_SIZE / kThreads;
+  int32_t tab[kTabPer];
+  {
+    const int32_t* tsrc = trow ? trow : lengths;
+    const int lim = trow ? ((n + NSA_PAGE_SIZE - 1) >> 6) - 1 : 0;
+#pragma unroll
+    for (int k = 0; k < kTabPer; ++k) tab[k] = tsrc[min(tid + k * kThreads, lim)];
+  }
 
   // ---- exact threshold among the candidates (bits 19..10, then 9..0)
   uint32_t prefix = bin << 20, pmask = 0xFFF00000u;
@@ -450,7 +485,12 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1u);
     }
     __syncthreads();
-    find_threshold_bin(hist, 1024, krem, s_sel);
+    {
+      const uint32_t c1[1] = {hist[tid]};
+      int tot1;
+      const int ex1 = block_exclusive_scan((int)c1[0], scan_buf, &tot1);
+      publish_threshold<1>(c1, (uint32_t)(tot1 - ex1) - c1[0], krem, s_sel);
+    }
     __syncthreads();
     prefix |= s_sel[0] << shift;
     pmask |= 1023u << shift;
@@ -471,7 +511,12 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
         atomicAdd(&hist[(tk >> shift) & (kTieBins - 1)], 1u);
     }
     __syncthreads();
-    find_threshold_bin(hist, kTieBins, krem, s_sel);
+    {
+      const uint32_t c1[1] = {tid < kTieBins ? hist[tid] : 0u};
+      int tot1;
+      const int ex1 = block_exclusive_scan((int)c1[0], scan_buf, &tot1);
+      publish_threshold<1>(c1, (uint32_t)(tot1 - ex1) - c1[0], krem, s_sel);
+    }
     __syncthreads();
     tprefix |= s_sel[0] << shift;
     tmask |= (uint32_t)(kTieBins - 1) << shift;
@@ -486,20 +531,28 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
     if (keep) atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
   }
   __syncthreads();
+  int32_t* ptab = reinterpret_cast<int32_t*>(cand_key);   // kCap >= 4096 entries
+  static_assert(kCap >= kTabPer * kThreads, "page table fits the candidate store");
+  if (trow) {
+#pragma unroll
+    for (int k = 0; k < kTabPer; ++k) ptab[tid + k * kThreads] = tab[k];
+  }
 
   // ---- kept positions in ascending order: each thread owns a run of words
+  // (the scan's barriers also publish the page table)
   const int per = (nw + kThreads - 1) / kThreads;
   const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
   int cnt = 0;
   for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
-  int tot;
-  int o = block_exclusive_scan(cnt, scan_buf, &tot);
+  int kept;
+  int o = block_exclusive_scan(cnt, scan_buf, &kept);
   for (int w = w0; w < w1; ++w) {
     uint32_t bits = bitmap[w];
     while (bits) {
       const int b = __ffs(bits) - 1;
       bits &= bits - 1;
-      if (o < topk) orow[o] = map(w * 32 + b);
+      const int i = w * 32 + b;
+      if (o < topk) orow[o] = trow ? (ptab[i >> 6] << 6) + (i & 63) : i;
       ++o;
     }
   }
