@@ -23,6 +23,8 @@
 // memory.
 #include "common.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int kThreads = 1024;
@@ -221,6 +223,16 @@ constexpr int kBatch = 4;           // float4 per thread per batch of the row pa
 
 static_assert(kMapBits == kTieBins * kTieBins, "tie radix spans the bitmap");
 
+// OR of w over the 8 lanes of the lane's aligned group of 8, in registers:
+// DPP quad_perm [1,0,3,2] and [2,3,0,1] combine each quad, row_half_mirror
+// (lane i of a half row reads lane 7 - i) then joins the group's two quads.
+__device__ __forceinline__ uint32_t or_lanes8(uint32_t w) {
+  w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0xB1, 0xF, 0xF, false);
+  w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x4E, 0xF, 0xF, false);
+  w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x141, 0xF, 0xF, false);
+  return w;
+}
+
 // Raw values of positions pos..pos+3 with no branch around the loads (a load
 // under a branch makes the compiler wait for every load in flight). VEC: one
 // 16-byte load at min(pos, vlast), where vlast is a multiple of 4 with
@@ -389,67 +401,84 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   }
 
   // ---- one pass over the row, batches of kBatch loads per thread, the next
-  // batch in flight while the current one is classified. Loads past the row
-  // are clamped onto its last vector, so the prefetch needs no branch.
-  const int lane = tid & 63;
+  // batch in flight while one is classified (two register batches used in
+  // turn). Loads past the row are clamped onto its last vector, so the
+  // prefetch needs no branch.
+  //
+  // The order key is monotone in the value (-0 == +0, NaN lowest), so for a
+  // bin strictly inside the finite range (8 <= bin <= 4087: bins 0..7 hold
+  // NaN and -inf, bins >= 4088 +inf and no finite value) "key >= K" is
+  // "x >= key_floor(K)", the smallest float with that key; the pass then
+  // compares floats and computes the key of candidates only.
   const int vend = VEC ? (n & ~3) : n;
   constexpr int kSpan = kThreads * 4;           // positions per load step
   constexpr int kPerBatch = kSpan * kBatch;
-  float cur[kBatch][4];
-  if (vend > 0) {   // VEC rows of 1..3 positions are all tail
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) load4<VEC>(row, j * kSpan + tid * 4, vend - 4, n, cur[j]);
-  }
-  for (int b0 = 0; b0 < vend; b0 += kPerBatch) {
-    float nxt[kBatch][4];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      load4<VEC>(row, b0 + kPerBatch + j * kSpan + tid * 4, vend - 4, n, nxt[j]);
-    uint32_t kb[kBatch][4];
-    int ce = 0;   // candidates of this thread in the batch
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int pos = b0 + j * kSpan + tid * 4;
-      uint32_t m = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kb[j][e] = order_key(cur[j][e]);
-        const bool in = pos + e < vend;
-        const uint32_t d = kb[j][e] >> 20;
-        m |= (in && d > bin) ? (1u << e) : 0u;
-        ce += (in && d == bin) ? 1 : 0;
-      }
-      if (m) atomicOr(&bitmap[pos >> 5], m << (pos & 31));
-    }
-    // one LDS atomic per wave reserves the wave's candidate slots
-    int incl = ce;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    int base = 0;
-    if (lane == 63 && incl > 0) base = atomicAdd(&s_ncand, incl);
-    base = __shfl(base, 63);
-    if (ce) {
-      int q = base + incl - ce;
+  auto key_floor = [](uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  };
+  const bool fcmp = bin >= 8 && bin <= 4087;
+  const float lo_bin = key_floor(bin << 20), lo_above = key_floor((bin + 1) << 20);
+  auto row_pass = [&](auto fc) {
+    constexpr bool FC = decltype(fc)::value;
+    auto above = [&](float x) {
+      if constexpr (FC) return x >= lo_above;
+      else return (order_key(x) >> 20) > bin;
+    };
+    auto in_bin = [&](float x) {
+      if constexpr (FC) return x >= lo_bin && !(x >= lo_above);
+      else return (order_key(x) >> 20) == bin;
+    };
+    // Classifies one batch: the bits of keys above the bin go straight into
+    // the bitmap (the 8 lanes sharing a 32-bit word OR their nibbles in
+    // registers and one of them stores it, so no LDS atomics), and the
+    // positions of keys in the bin are appended to the candidate store (a
+    // loop over the set bits of a 16-bit mask; the keys are read back after
+    // the pass).
+    auto classify = [&](const float (&v)[kBatch][4], int b0) {
+      uint32_t cm = 0;   // bit 4j + e: candidate
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int pos = b0 + j * kSpan + tid * 4;
+        uint32_t m = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (pos + e < vend && (kb[j][e] >> 20) == bin) {
-            if (q < kCap) { cand_key[q] = kb[j][e]; cand_pos[q] = pos + e; }
-            ++q;
-          }
+          const bool in = pos + e < vend;
+          m |= (in && above(v[j][e])) ? (1u << e) : 0u;
+          cm |= (in && in_bin(v[j][e])) ? (1u << (4 * j + e)) : 0u;
         }
+        const uint32_t w = or_lanes8(m << ((tid & 7) * 4));
+        const int word = pos >> 5;
+        if ((tid & 7) == 0 && word < kMapWords) bitmap[word] = w;
       }
+      // a lane with candidates reserves its slots with one LDS atomic (the
+      // order of the candidates does not matter to the exact selection)
+      int q = 0;
+      if (cm) q = atomicAdd(&s_ncand, __popc(cm));
+      while (cm) {
+        const int b = __ffs(cm) - 1;
+        cm &= cm - 1;
+        if (q < kCap) cand_pos[q] = b0 + (b >> 2) * kSpan + tid * 4 + (b & 3);
+        ++q;
+      }
+    };
+    if (vend <= 0) return;   // VEC rows of 1..3 positions are all tail
+    float va[kBatch][4], vb[kBatch][4];
+    auto fetch = [&](float (&v)[kBatch][4], int b0) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        load4<VEC>(row, b0 + j * kSpan + tid * 4, vend - 4, n, v[j]);
+    };
+    fetch(va, 0);
+    for (int b0 = 0; b0 < vend; b0 += 2 * kPerBatch) {
+      fetch(vb, b0 + kPerBatch);
+      classify(va, b0);
+      fetch(va, b0 + 2 * kPerBatch);
+      classify(vb, b0 + kPerBatch);     // positions past vend are masked
     }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cur[j][e] = nxt[j][e];
-  }
+  };
+  if (fcmp) row_pass(std::true_type{});
+  else row_pass(std::false_type{});
+  __syncthreads();   // every bitmap word of the pass is stored
   if (VEC && tid < n - vend) {   // the 0..3 positions past the last vector
     const int pos = vend + tid;
     const uint32_t k = order_key(row[pos]);
@@ -457,11 +486,13 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
       atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
     } else if ((k >> 20) == bin) {
       const int q = atomicAdd(&s_ncand, 1);
-      if (q < kCap) { cand_key[q] = k; cand_pos[q] = pos; }
+      if (q < kCap) cand_pos[q] = pos;
     }
   }
   __syncthreads();
   const int nc = min(s_ncand, kCap);
+  // keys of the candidates, read back from the row (just read, so cached)
+  for (int i = tid; i < nc; i += kThreads) cand_key[i] = order_key(row[cand_pos[i]]);
   // the row's page-table entries for the output, loaded now (branch-free:
   // without a table the loads read lengths[0]) and put in LDS once the
   // candidates are no longer needed

@@ -29,10 +29,21 @@ def _topk_rows(rng, lengths, width, kind):
             v[rng.random(L) < 0.01] = np.inf
             v[rng.random(L) < 0.1] = -0.0
             x[t, :L] = v
+        elif kind == "neg_inf_heavy":   # threshold in the -inf / NaN bins
+            v = rng.normal(size=L).astype(np.float32)
+            r = rng.random(L)
+            v[r < 0.97] = -np.inf
+            v[r < 0.02] = np.nan
+            x[t, :L] = v
+        elif kind == "pos_inf_heavy":   # threshold in the +inf bin
+            v = rng.normal(size=L).astype(np.float32)
+            v[rng.random(L) < 0.3] = np.inf
+            x[t, :L] = v
     return x
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "const", "special"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "const", "special", "neg_inf_heavy",
+                                  "pos_inf_heavy"])
 @pytest.mark.parametrize("topk", [256, 2048])
 @pytest.mark.parametrize("pad", [6, 67])   # odd row stride: scalar loads; else vector
 def test_topk_exact_on_given_logits(kind, topk, pad):
