@@ -8,7 +8,10 @@
 // chain of torch ops plus a host sync for max(seq_lens); here one kernel
 // writes all of them with the bound given by the host.
 //
-// Launch shape: one 256-thread block per request. A block needs three
+// Launch shape: one 256-thread block per request for the lengths, then one
+// block per (request, 256 page columns) for the page tables (a block per
+// request alone gathering 2048 strided entries was bound by one CU's memory
+// throughput). A request's block needs three
 // exclusive prefix sums over the requests before it (KV lengths, query
 // rows, clipped lengths); it recomputes them itself (O(bs) per block), which
 // avoids a second launch or a grid-wide barrier. The clipped-length sum of
@@ -72,8 +75,28 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
                       int32_t* token_to_req, int32_t* page_table_1,
                       int64_t pt1_stride) {
   __shared__ long long red[3 * (kThreads / 64)];
-  const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  const int nreq_blocks = bs > 0 ? bs : 1;
+  if ((int)blockIdx.x >= nreq_blocks) {
+    // page tables: request r, page columns c*kThreads .. (one per thread);
+    // the compact entry is every 64th token slot divided by 64 (arithmetic
+    // shift = floor division), the wide table copies the 64 token slots
+    const int ncols = (max_seqlen_k + NSA_PAGE_SIZE - 1) / NSA_PAGE_SIZE;
+    const int chunks = (ncols + kThreads - 1) / kThreads;
+    const int b = blockIdx.x - nreq_blocks;
+    const int r = b / chunks, c = b % chunks;
+    const int32_t* row = req_to_token + (int64_t)req_pool_indices[r] * rtt_stride;
+    const int p = c * kThreads + tid;
+    if (p < ncols) real_page_table[(int64_t)r * rpt_stride + p] = row[(int64_t)p * NSA_PAGE_SIZE] >> 6;
+    if (page_table_1 != nullptr) {
+      int32_t* pt = page_table_1 + (int64_t)r * pt1_stride;
+      const int c0 = c * kThreads * NSA_PAGE_SIZE;
+      const int c1 = min(c0 + kThreads * NSA_PAGE_SIZE, max_seqlen_k);
+      for (int k = c0 + tid; k < c1; k += kThreads) pt[k] = row[k];
+    }
+    return;
+  }
+  const int r = blockIdx.x;
   const int d = (mode == NSA_MODE_TARGET_VERIFY) ? draft : 0;
 
   // exclusive prefix sums over requests 0..r-1
@@ -116,31 +139,6 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
     if (mode != NSA_MODE_EXTEND) cu_seqlens_q[t + 1] = (int32_t)(t + 1);
   }
 
-  // page-granular table: every 64th entry of the request's token table,
-  // divided by 64 (arithmetic shift = floor division)
-  const int32_t* row = req_to_token + (int64_t)req_pool_indices[r] * rtt_stride;
-  const int ncols = (max_seqlen_k + NSA_PAGE_SIZE - 1) / NSA_PAGE_SIZE;
-  int32_t* rpt = real_page_table + (int64_t)r * rpt_stride;
-  // strided gather (one cache line per entry): up to 8 loads in flight per
-  // thread, all issued before any is stored
-  constexpr int kBatch = 8;
-  for (int p0 = 0; p0 < ncols; p0 += kThreads * kBatch) {
-    int32_t v[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int p = p0 + b * kThreads + tid;
-      v[b] = row[(int64_t)min(p, ncols - 1) * NSA_PAGE_SIZE];
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int p = p0 + b * kThreads + tid;
-      if (p < ncols) rpt[p] = v[b] >> 6;
-    }
-  }
-  if (page_table_1 != nullptr) {
-    int32_t* pt = page_table_1 + (int64_t)r * pt1_stride;
-    for (int c = tid; c < max_seqlen_k; c += kThreads) pt[c] = row[c];
-  }
 }
 
 }  // namespace
@@ -197,8 +195,10 @@ extern "C" int nsa_build_metadata(
   NSA_REQUIRE(page_table_1 == nullptr || pt1_stride >= max_seqlen_k,
               NSA_ERR_INVALID_ARG, "%s: pt1_stride < max_seqlen_k", fn);
 
-  const int grid = bs > 0 ? bs : 1;
-  hipLaunchKernelGGL(build_metadata_kernel, dim3(grid), dim3(kThreads), 0,
+  const int64_t chunks = (ncols + kThreads - 1) / kThreads;
+  const int64_t grid = (bs > 0 ? bs : 1) + (int64_t)bs * chunks;
+  NSA_REQUIRE(grid < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  hipLaunchKernelGGL(build_metadata_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, mode, bs, draft_token_num, topk,
                      seq_lens, extend_lens, req_to_token, rtt_stride,
                      req_pool_indices, max_seqlen_k, num_q_rows, cache_seqlens,
