@@ -357,6 +357,22 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   }
   const float* row = logits + t * logits_stride;
 
+  // the first batch of the row pass does not depend on the threshold: its
+  // loads are issued now and land while the histogram is read and scanned
+  const int vend = VEC ? (n & ~3) : n;
+  constexpr int kSpan = kThreads * 4;           // positions per load step
+  constexpr int kPerBatch = kSpan * kBatch;
+  // last vector start; n >= 1 here, and a vector row (16-byte aligned,
+  // stride a multiple of 4) always holds positions 0..3, so 0 is a safe
+  // clamp for rows shorter than one vector
+  const int vlast = vend >= 4 ? vend - 4 : 0;
+  float va[kBatch][4], vb[kBatch][4];
+  auto fetch = [&](float (&v)[kBatch][4], int b0) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) load4<VEC>(row, b0 + j * kSpan + tid * 4, vlast, n, v[j]);
+  };
+  fetch(va, 0);   // no branch: a load under one would be waited for at once
+
   // ---- row histogram of the top 12 key bits and its threshold bin: each
   // thread owns 4 bins in registers (given, then cleared; or summed over the
   // chunks of pass 1 with 8-byte loads); one block scan gives the total and,
@@ -410,9 +426,6 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   // NaN and -inf, bins >= 4088 +inf and no finite value) "key >= K" is
   // "x >= key_floor(K)", the smallest float with that key; the pass then
   // compares floats and computes the key of candidates only.
-  const int vend = VEC ? (n & ~3) : n;
-  constexpr int kSpan = kThreads * 4;           // positions per load step
-  constexpr int kPerBatch = kSpan * kBatch;
   auto key_floor = [](uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
   };
@@ -462,13 +475,6 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
       }
     };
     if (vend <= 0) return;   // VEC rows of 1..3 positions are all tail
-    float va[kBatch][4], vb[kBatch][4];
-    auto fetch = [&](float (&v)[kBatch][4], int b0) {
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        load4<VEC>(row, b0 + j * kSpan + tid * 4, vend - 4, n, v[j]);
-    };
-    fetch(va, 0);
     for (int b0 = 0; b0 < vend; b0 += 2 * kPerBatch) {
       fetch(vb, b0 + kPerBatch);
       classify(va, b0);
