@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b128",
-                    choices=["decode_b128", "decode_b32", "verify", "extend"])
+                    choices=["decode_b128", "decode_b32", "verify", "extend",
+                             "draft_extend", "draft_extend_v2"])
     ap.add_argument("--cpu-rows", type=int, default=40,
                     help="rows of the oracle sample (0 = skip the CPU leg)")
     ap.add_argument("--seed", type=int, default=0)
