@@ -212,7 +212,8 @@ def main():
         nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
                                md["real_page_table"], md["token_to_req"],
                                md["seqlens_expanded"], w.max_seqlen_k,
-                               logits=logits, dtype=idt, key_hist=key_hist)
+                               logits=logits, dtype=idt, key_hist=key_hist,
+                               rows_per_request=max(w.draft, 1))
         if e: e[2].record()
         nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                w.max_seqlen_k, table=md["real_page_table"],

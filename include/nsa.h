@@ -208,6 +208,13 @@ int nsa_topk_transform(const float* logits, int64_t logits_stride,
  * x >= 0 and all bits inverted for x < 0 (so keys order as the floats).
  * key_hist is device memory of T * 4096 uint32, 4-byte aligned, owned by the
  * caller, and must hold zeros on entry (counts are added atomically).
+ * rows_per_request: a scheduling hint, not a change of results. When rows
+ * come in fixed groups of this many consecutive rows of one request
+ * (target-verify and draft-extend-v2 layouts: draft_token_num) and T is a
+ * multiple of it, the blocks of a group that read the same key pages run
+ * back to back on one XCD, so the pages are fetched from HBM about once per
+ * group; any other value (1, or rows that do not form such groups) gives
+ * the same logits and counts with the per-row order.
  *
  * nsa_topk_transform_hist: as nsa_topk_transform, with key_hist from
  * nsa_indexer_logits_hist over the same logits (16-byte aligned); it needs
@@ -224,7 +231,8 @@ int nsa_indexer_logits_hist(const void* q, int q_dtype, const float* weights,
                             const int32_t* seqlens_expanded, int T, int Hi,
                             int Di, int page_size, int max_seqlen_k,
                             float* logits, int64_t logits_stride,
-                            uint32_t* key_hist, void* stream);
+                            uint32_t* key_hist, int rows_per_request,
+                            void* stream);
 int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
                             const int32_t* lengths, int T, int topk,
                             int max_seqlen_k, const int32_t* table,

@@ -139,11 +139,14 @@ def new_key_hist(T, device):
 
 def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits=None,
-                       dtype=DTYPE_FP8_E4M3, key_hist=None):
+                       dtype=DTYPE_FP8_E4M3, key_hist=None, rows_per_request=1):
     """Indexer logits [T, >= max_seqlen_k] fp32 (positions past each row's
     length are left unwritten). ``q``: [T, Hi, Di] uint8 fp8 codes (dtype
     DTYPE_FP8_E4M3) or float32 (DTYPE_FP32). With ``key_hist`` (zeroed, see
-    new_key_hist) the logits' top-k histogram is counted in the same pass."""
+    new_key_hist) the logits' top-k histogram is counted in the same pass,
+    and ``rows_per_request`` (draft_token_num for target-verify and
+    draft-extend v2) lets a request's rows share their key-page reads; it
+    does not change the results."""
     _check(q, "q", torch.uint8 if dtype == DTYPE_FP8_E4M3 else torch.float32, 3)
     _check(weights, "weights", torch.float32, 2)
     _check(index_cache, "index_cache", torch.uint8, 2)
@@ -165,7 +168,8 @@ def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
         _check(key_hist, "key_hist", torch.int32, 2)
         if key_hist.shape[0] < T or key_hist.shape[1] != KEY_BINS:
             raise ValueError("key_hist must be [>= T, 4096]")
-        call("nsa_indexer_logits_hist", *args, _ptr(key_hist), _stream())
+        call("nsa_indexer_logits_hist", *args, _ptr(key_hist), int(rows_per_request),
+             _stream())
     return logits
 
 

@@ -21,7 +21,7 @@ SIGNATURES = {
         c_int, c_int, P, c_i64, P]),
     "nsa_indexer_logits_hist": (c_int, [
         P, c_int, P, P, c_int, c_i64, P, c_i64, P, P, c_int, c_int, c_int,
-        c_int, c_int, P, c_i64, P, P]),
+        c_int, c_int, P, c_i64, P, c_int, P]),
     "nsa_topk_workspace_size": (c_int, [c_int, c_int, c_int, ctypes.POINTER(c_size)]),
     "nsa_topk_transform_hist": (c_int, [
         P, c_i64, P, c_int, c_int, c_int, P, c_i64, P, c_int, P, P, c_i64, P]),

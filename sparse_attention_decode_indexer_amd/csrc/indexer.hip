@@ -15,6 +15,11 @@
 //     different XCD than the previous row's and rows of unequal length
 //     spread evenly (an even count pins chunk c to XCD c mod 8, and the
 //     XCDs holding the low chunks, which every row has, finish last);
+//   * rows that share a request in fixed groups (target-verify, draft-extend
+//     v2: `group` consecutive rows per request) read the same pages: their
+//     blocks for one chunk are made consecutive on one XCD (work group b
+//     runs on XCD b % 8), so the first fills that XCD's L2 and the others
+//     hit it;
 //   * wave w takes pages
 //     w, w+4, ... of the chunk, so a wave always works on a whole page
 //     (64 tokens = 8 KB of keys + 256 B of scales, contiguous); two page
@@ -77,10 +82,17 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    const int32_t* __restrict__ t2r,
                    const int32_t* __restrict__ seqlens, int max_seqlen_k,
                    float* __restrict__ logits, int64_t logits_stride,
-                   int chunks_per_row, uint32_t* __restrict__ key_hist) {
+                   int chunks_per_row, int group, int64_t npairs,
+                   uint32_t* __restrict__ key_hist) {
   __shared__ uint32_t lhist[HIST ? kKeyBins : 1];
-  const int64_t t = blockIdx.x / chunks_per_row;
-  const int chunk = blockIdx.x % chunks_per_row;
+  // block -> (row group, chunk) pair qi and row j of the group: the blocks
+  // of one pair are `group` consecutive slots of one XCD's sequence (for
+  // group 1 this is the plain order, qi = blockIdx.x)
+  const int64_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int64_t qi = (slot / group) * 8 + xcd;
+  if (qi >= npairs) return;
+  const int64_t t = (qi / chunks_per_row) * group + slot % group;
+  const int chunk = (int)(qi % chunks_per_row);
   int L = seqlens[t];
   L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
   const int npages = (L + kPage - 1) / kPage;
@@ -237,7 +249,7 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
                 const int32_t* token_to_req, const int32_t* seqlens_expanded,
                 int T, int Hi, int Di, int page_size, int max_seqlen_k,
                 float* logits, int64_t logits_stride, uint32_t* key_hist,
-                void* stream) {
+                int rows_per_request, void* stream) {
   NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0 && num_pages >= 0,
               NSA_ERR_INVALID_ARG, "%s: negative size", fn);
   NSA_REQUIRE(page_size == NSA_PAGE_SIZE, NSA_ERR_UNSUPPORTED,
@@ -272,9 +284,11 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
               NSA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   hipStream_t s = (hipStream_t)stream;
   if (fp8) {
-    // odd, so that consecutive rows start on different XCDs
+    // odd, so that consecutive rows (row groups) start on different XCDs
     const int chunks = (int)((ncols + kPagesPerBlock - 1) / kPagesPerBlock) | 1;
-    const int64_t blocks = (int64_t)T * chunks;
+    const int group = (rows_per_request > 1 && T % rows_per_request == 0) ? rows_per_request : 1;
+    const int64_t npairs = (int64_t)(T / group) * chunks;
+    const int64_t blocks = (npairs + 7) / 8 * 8 * group;
     NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
     auto kern = key_hist ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0,
@@ -282,7 +296,7 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
                        static_cast<const uint8_t*>(k_index_cache), num_pages,
                        real_page_table, rpt_stride, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits, logits_stride,
-                       chunks, key_hist);
+                       chunks, group, npairs, key_hist);
   } else {
     const int chunks = (max_seqlen_k + 255) / 256;
     const int64_t blocks = (int64_t)T * chunks;
@@ -314,7 +328,7 @@ extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
   return indexer_run("nsa_indexer_logits", q, q_dtype, weights, k_index_cache,
                      k_dtype, num_pages, real_page_table, rpt_stride,
                      token_to_req, seqlens_expanded, T, Hi, Di, page_size,
-                     max_seqlen_k, logits, logits_stride, nullptr, stream);
+                     max_seqlen_k, logits, logits_stride, nullptr, 1, stream);
 }
 
 extern "C" int nsa_indexer_logits_hist(const void* q, int q_dtype,
@@ -328,12 +342,12 @@ extern "C" int nsa_indexer_logits_hist(const void* q, int q_dtype,
                                        int Hi, int Di, int page_size,
                                        int max_seqlen_k, float* logits,
                                        int64_t logits_stride, uint32_t* key_hist,
-                                       void* stream) {
+                                       int rows_per_request, void* stream) {
   const char* fn = "nsa_indexer_logits_hist";
   NSA_REQUIRE(T == 0 || key_hist != nullptr, NSA_ERR_INVALID_ARG,
               "%s: null key_hist", fn);
   return indexer_run(fn, q, q_dtype, weights, k_index_cache, k_dtype, num_pages,
                      real_page_table, rpt_stride, token_to_req, seqlens_expanded,
                      T, Hi, Di, page_size, max_seqlen_k, logits, logits_stride,
-                     key_hist, stream);
+                     key_hist, rows_per_request, stream);
 }

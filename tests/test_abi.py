@@ -168,11 +168,11 @@ def test_fused_histogram_entry_points_validate(lib):
     P = ctypes.c_void_p
     # null key_hist
     assert lib.nsa_indexer_logits_hist(P(16), 2, P(16), P(16), 2, 10, P(16), 4, P(16),
-                                       P(16), 1, 64, 128, 64, 256, P(16), 256, N, N) == -1
+                                       P(16), 1, 64, 128, 64, 256, P(16), 256, N, 1, N) == -1
     assert "key_hist" in _err(lib)
     # the histogram needs the fp8 path
     assert lib.nsa_indexer_logits_hist(P(16), 0, P(16), P(16), 0, 10, P(16), 4, P(16),
-                                       P(16), 1, 4, 64, 64, 256, P(16), 256, P(16), N) == -2
+                                       P(16), 1, 4, 64, 64, 256, P(16), 256, P(16), 1, N) == -2
     # misaligned key_hist for the top-k
     assert lib.nsa_topk_transform_hist(P(16), 256, P(16), 1, 64, 256, N, 0, N, 64,
                                        P(18), P(16), 64, N) == -1

@@ -22,7 +22,8 @@ def run_path(nsa, w, fused=True, hist=False):
     logits = nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
                                     md["real_page_table"], md["token_to_req"],
                                     md["seqlens_expanded"], w.max_seqlen_k,
-                                    dtype=idx_dtype(nsa, w), key_hist=kh)
+                                    dtype=idx_dtype(nsa, w), key_hist=kh,
+                                    rows_per_request=max(w.draft, 1))
     logical = nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                      w.max_seqlen_k, key_hist=kh)
     if hist:
@@ -157,3 +158,30 @@ def test_fused_histogram_exact_and_topk_identical(name):
     again = nsa.nsa_topk_transform(*args, key_hist=kh, **kw)
     torch.cuda.synchronize()
     assert torch.equal(plain, again)
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("verify", dict(bs=6, seqlen_range=(3000, 40000))),
+    ("draft_extend_v2", dict(bs=5, seqlen_range=(3000, 40000))),
+    ("decode_b32", dict(bs=7)),
+])
+def test_indexer_row_groups_change_nothing(name, overrides):
+    # grouping the rows of a request only reorders the blocks: logits and
+    # histogram counts are identical (ungrouped, grouped, and a group size
+    # that does not match the layout)
+    nsa = need_gpu()
+    w = W.make_workload(name, device=DEV, parts=("indexer",), **overrides)
+    md = gpu_metadata(nsa, w)
+    outs = []
+    for g in (1, max(w.draft, 1), 3):
+        kh = nsa.new_key_hist(w.num_rows, DEV)
+        lg = torch.full((w.num_rows, nsa.logits_row_stride(w.max_seqlen_k)), 7.0,
+                        device=DEV)
+        nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
+                               md["real_page_table"], md["token_to_req"],
+                               md["seqlens_expanded"], w.max_seqlen_k, logits=lg,
+                               key_hist=kh, rows_per_request=g)
+        torch.cuda.synchronize()
+        outs.append((lg.cpu(), kh.cpu()))
+    for lg, kh in outs[1:]:
+        assert torch.equal(lg, outs[0][0]) and torch.equal(kh, outs[0][1])
