@@ -9,8 +9,9 @@ before timing starts.
 
 Prints one JSON line. `value` is query rows (tokens) per second over the
 timed steps; `roofline` is for the dominant kernel (the indexer), with its
-algorithmic bytes per launch divided by its average launch time, measured
-with HIP events on the launch stream; `cpu_baseline` is the CPU oracle timed
+algorithmic bytes (or, where its fp8 dot products take longer at peak than
+its bytes, its flops) per launch divided by its average launch time,
+measured with HIP events on the launch stream; `cpu_baseline` is the CPU oracle timed
 on a bounded sample of rows of the same workload.
 """
 
@@ -25,8 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0     # dense fp8 MFMA
 METRIC = "query-tokens/s through indexer+topk+sparse MLA; % of HBM roofline"
 PMC_FILE = os.path.join(ROOT, "profiles", "indexer_fp8_decode_b128_pmc.txt")
+PMC_WORKLOAD = "decode_b128"
 
 
 def parse():
@@ -46,26 +49,33 @@ def parse():
     return ap.parse_args()
 
 
-def indexer_bytes(lengths, hi=64, di=128):
-    """Algorithmic bytes of one indexer launch: per row the q row and weights,
-    one page-table entry per 64 positions, and per position the fp8 key,
-    its fp32 scale and the fp32 logit written."""
-    b = 0
-    for L in lengths:
+def indexer_cost(lengths, t2r, hi=64, di=128):
+    """Algorithmic bytes and flops of one indexer launch. Bytes: per row its
+    q row and weights and the fp32 logit of every position; per request the
+    fp8 key and fp32 scale of every position its longest row sees, and one
+    page-table entry per 64 of them (rows of one request read the same keys,
+    which need to come from HBM once). Flops: 2 * hi * di per (row,
+    position) for the dot products."""
+    longest = {}
+    b = fl = 0
+    for L, r in zip(lengths, t2r):
         L = int(L)
-        b += hi * di + hi * 4 + ((L + 63) // 64) * 4 + L * (di + 4 + 4)
-    return b
+        b += hi * di + hi * 4 + L * 4
+        fl += 2 * hi * di * L
+        longest[int(r)] = max(longest.get(int(r), 0), L)
+    for L in longest.values():
+        b += L * (di + 4) + ((L + 63) // 64) * 4
+    return b, fl
 
 
-def pipeline_bytes(lengths, topk, heads, kv_row_bytes, hi=64, di=128):
-    """Strict algorithmic bytes of one step: index keys + scales, q / w, the
-    page-table row, the selected latent rows, MLA q and output."""
-    b = 0
+def pipeline_bytes(lengths, t2r, topk, heads, kv_row_bytes, hi=64, di=128):
+    """Strict algorithmic bytes of one step: the indexer's (keys once per
+    request), then per row the selected latent rows, MLA q and output."""
+    b, _ = indexer_cost(lengths, t2r, hi, di)
     for L in lengths:
         L = int(L)
-        n = min(L, topk)
-        b += hi * di + hi * 4 + ((L + 63) // 64) * 4 + L * (di + 4)
-        b += n * kv_row_bytes + heads * 576 * 2 + heads * 512 * 2 + heads * 4
+        b -= L * 4                               # logits are not strict bytes
+        b += min(L, topk) * kv_row_bytes + heads * 576 * 2 + heads * 512 * 2 + heads * 4
     return b
 
 
@@ -213,7 +223,7 @@ def main():
                                md["real_page_table"], md["token_to_req"],
                                md["seqlens_expanded"], w.max_seqlen_k,
                                logits=logits, dtype=idt, key_hist=key_hist,
-                               rows_per_request=max(w.draft, 1))
+                               rows_per_request=w.rows_per_request)
         if e: e[2].record()
         nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                w.max_seqlen_k, table=md["real_page_table"],
@@ -253,15 +263,29 @@ def main():
     stage_ms = stage.mean(axis=0)
     ms_per_step = elapsed * 1e3 / args.steps
     se = md["seqlens_expanded"].cpu().numpy()     # visible length of every row
-    idx_bytes = indexer_bytes(se, w.idx_heads, w.idx_dim)
+    t2r = md["token_to_req"].cpu().numpy()
+    idx_bytes, idx_flops = indexer_cost(se, t2r, w.idx_heads, w.idx_dim)
     idx_ms = stage_ms[1]
-    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
-    pipe = pipeline_bytes(se, w.topk, w.heads, 656 if fp8_kv else 1152,
+    # the indexer's bound: HBM for its bytes or fp8 MFMA for its dot
+    # products, whichever takes longer at peak
+    if idx_flops / FP8_PEAK_TFLOPS > idx_bytes / HBM_PEAK_GBPS * 1e3:
+        roof = {"bound": "mfma", "achieved": idx_flops / (idx_ms * 1e-3) / 1e12,
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": idx_bytes / (idx_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    pipe = pipeline_bytes(se, t2r, w.topk, w.heads, 656 if fp8_kv else 1152,
                           w.idx_heads, w.idx_dim)
     pipe_gbps = pipe / (ms_per_step * 1e-3) / 1e9
     src = open(os.path.join(ROOT, "sparse_attention_decode_indexer_amd", "csrc",
                             "indexer.hip"), "rb").read()
-    traffic = read_pmc(hashlib.sha256(src).hexdigest())
+    # the committed counters were taken on the default decode workload
+    traffic = (read_pmc(hashlib.sha256(src).hexdigest())
+               if args.workload == PMC_WORKLOAD else None)
+    grouped = idt == nsa.DTYPE_FP8_E4M3 and w.rows_per_request >= 4
+    kernel = ("indexer_fp8_rows_kernel" if grouped else
+              "indexer_fp8_kernel" if idt == nsa.DTYPE_FP8_E4M3 else "indexer_fp32_kernel")
 
     res = {
         "metric": METRIC,
@@ -281,11 +305,9 @@ def main():
                    "mla_heads": w.heads, "kv_cache": w.kv_kind,
                    "indexer": f"{w.idx_heads}x{w.idx_dim} {w.idx_kind}",
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "indexer_fp8_kernel", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": idx_bytes},
+        "roofline": dict(kernel=kernel, **roof, traffic=traffic,
+                         algorithmic_bytes_per_launch=idx_bytes,
+                         algorithmic_flops_per_launch=idx_flops),
         "pipeline": {"algorithmic_bytes_per_step": pipe, "GBps": pipe_gbps,
                      "hbm_roofline_frac": pipe_gbps / HBM_PEAK_GBPS},
         "stages_ms": {"metadata": stage_ms[0], "indexer": stage_ms[1],

@@ -149,11 +149,16 @@ int nsa_build_metadata(int mode, int bs, int draft_token_num, int topk,
  *                    NSA_DTYPE_FP8_E4M3) or fp32 (NSA_DTYPE_FP32). Any
  *                    query-side scale is folded into weights by the caller.
  *   weights          [T, Hi] fp32.
+ *                    q, weights and the keys are finite (fp8 NaN codes
+ *                    0x7F / 0xFF are outside the contract: their logits
+ *                    are unspecified).
  *   k_index_cache    [num_pages] pages of 64 tokens; page bytes =
  *                    64*Di*elem (keys, row-major [64][Di]) + 64*4 (fp32
  *                    per-token scales). k_dtype must equal q_dtype.
  *   real_page_table  [*, rpt_stride] page ids per request; a page id outside
  *                    [0, num_pages) yields -inf logits for its 64 positions.
+ *                    The fp8 path needs num_pages >= 1 (it reads page 0 in
+ *                    place of an absent page); 0 is NSA_ERR_INVALID_ARG there.
  *   token_to_req[T], seqlens_expanded[T]  from nsa_build_metadata.
  *   logits           [T, logits_stride] fp32, logits_stride >= max_seqlen_k.
  *                    Rows that start 256-byte aligned (stride a multiple of
@@ -208,13 +213,17 @@ int nsa_topk_transform(const float* logits, int64_t logits_stride,
  * x >= 0 and all bits inverted for x < 0 (so keys order as the floats).
  * key_hist is device memory of T * 4096 uint32, 4-byte aligned, owned by the
  * caller, and must hold zeros on entry (counts are added atomically).
- * rows_per_request: a scheduling hint, not a change of results. When rows
- * come in fixed groups of this many consecutive rows of one request
- * (target-verify and draft-extend-v2 layouts: draft_token_num) and T is a
- * multiple of it, the blocks of a group that read the same key pages run
- * back to back on one XCD, so the pages are fetched from HBM about once per
- * group; any other value (1, or rows that do not form such groups) gives
- * the same logits and counts with the per-row order.
+ * rows_per_request: a scheduling hint (the typical number of consecutive
+ * rows of one request), not a change of results:
+ *   >= 4     rows are scored in groups of 4 consecutive rows; a group whose
+ *            rows share one request reads each key page once for all of
+ *            them (target-verify, draft-extend v2 with 4 drafts, extend),
+ *            a group that mixes requests scores its rows one at a time;
+ *   2 or 3   when T is a multiple of it, the blocks of a group that read
+ *            the same key pages run back to back on one XCD, so the pages
+ *            come from HBM about once per group;
+ *   other    per-row order.
+ * Every choice gives bit-identical logits and counts.
  *
  * nsa_topk_transform_hist: as nsa_topk_transform, with key_hist from
  * nsa_indexer_logits_hist over the same logits (16-byte aligned); it needs

@@ -24,7 +24,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # IEEE fp32 division for the fp8 cache encoder (x / scale)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed fp32 arithmetic in generated code
@@ -33,21 +32,48 @@ FLAGS = [
     "-Wno-unused-function",
 ]
 
+# Per-source additions. The indexer consumes every MFMA result in VALU code
+# at once: MFMAs that write VGPRs save one v_accvgpr_read per output value
+# (the attention kernel keeps its accumulators in AGPRs on purpose, so the
+# option is not global).
+SOURCE_FLAGS = {
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
-def build_library(verbose=False, extra_flags=()):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *srcs,
-           "-o", tmp]
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                            text=True)
+
+
+def _finish(proc, what, verbose):
+    text, _ = proc.communicate()
+    out = "\n".join(line for line in text.splitlines()
                     if "packed-fp32-ops" not in line)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build_library(verbose=False, extra_flags=()):
+    """Compiles every source to an object (in parallel), then links them."""
+    objdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-I", INCLUDE,
+               "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        objs.append(obj)
+        procs.append((_run(cmd, verbose), src))
+    for proc, src in procs:
+        _finish(proc, src, verbose)
+    tmp = LIB_PATH + ".tmp"
+    _finish(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                 verbose), "link", verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

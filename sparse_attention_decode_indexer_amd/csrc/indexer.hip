@@ -71,6 +71,15 @@ __device__ __forceinline__ void load_page(PageKeys& pk, const uint8_t* base,
   pk.ks = *reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane);
 }
 
+// ReLU as one integer max on the float's bits: a negative value (sign bit
+// set) is a negative int and becomes +0, a positive one is unchanged.
+// fmaxf costs two instructions (the compiler first quiets a possible NaN).
+// The dot products are finite for finite fp8 codes; a NaN code gives NaN
+// or 0 here, and NaN logits are outside the contract.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // HIST: also count the top 12 bits of every written logit's order key into
 // key_hist[t][0..4095] (an LDS histogram per block, then one global atomic
 // per nonzero bin), so the top-k needs no pass of its own to histogram.
@@ -156,7 +165,7 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
         const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             qa[ht], pk.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s = fmaf(wr[ht][r], fmaxf(acc[r], 0.0f), s);
+        for (int r = 0; r < 4; ++r) s = fmaf(wr[ht][r], relu(acc[r]), s);
       }
       v[j] = s;
     }
@@ -195,6 +204,183 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
       if (v.y) atomicAdd(&dst[4 * i + 1], v.y);
       if (v.z) atomicAdd(&dst[4 * i + 2], v.z);
       if (v.w) atomicAdd(&dst[4 * i + 3], v.w);
+    }
+  }
+}
+
+// Rows that share a request (target-verify, draft-extend v2, extend) read the
+// same key pages. This kernel scores each page once for kRows consecutive
+// rows: a block takes (group of kRows rows, chunk of 32 pages) and every
+// wave scores its page buffer against all rows of the group, so the key
+// bytes read per row drop kRows-fold and MFMA work per byte rises as much.
+// q (8 KB per row) and the head weights of the group sit in LDS instead of
+// registers; the MFMA operands, the order of the ReLU-weight FMAs and the
+// transpose-reduce are those of indexer_fp8_kernel, so each row's logits are
+// bit-identical to the one-row kernel's. A group whose rows belong to
+// different requests is scored one row per pass over that row's pages.
+// It always builds the rows' key histograms (the fused top-k input) and
+// serves the histogram entry point only.
+constexpr int kRows = 4;
+constexpr int kQRowBytes = kHeads * kDim;  // 8192
+
+// LDS offset of 16-byte piece `piece` of head h's q row: pieces are rotated by
+// (h >> 1) & 7, so the 16 lanes of one ds_read_b128 (heads c = 0..15 of a
+// tile, one piece) cover all 64 banks once.
+__device__ __forceinline__ int q_lds(int h, int piece) {
+  return h * kDim + ((piece ^ ((h >> 1) & 7)) << 4);
+}
+
+__global__ void __launch_bounds__(256)
+indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
+                        const uint8_t* __restrict__ cache, int64_t num_pages,
+                        const int32_t* __restrict__ rpt, int64_t rpt_stride,
+                        const int32_t* __restrict__ t2r,
+                        const int32_t* __restrict__ seqlens, int max_seqlen_k,
+                        int64_t T, float* __restrict__ logits,
+                        int64_t logits_stride, int chunks_per_group,
+                        uint32_t* __restrict__ key_hist) {
+  __shared__ __align__(16) uint8_t sq[kRows * kQRowBytes];
+  __shared__ __align__(16) float sw[kRows * kHeads];
+  // two 16-bit counts per word: a block writes at most 2048 logits per row
+  __shared__ __align__(16) uint32_t lhist[kRows * kKeyBins / 2];
+
+  const int64_t t0 = (int64_t)(blockIdx.x / chunks_per_group) * kRows;
+  const int chunk = (int)(blockIdx.x % chunks_per_group);
+  const int nrows = (int)min<int64_t>(kRows, T - t0);
+  int Lr[kRows];
+  int req[kRows];
+  bool uniform = true;
+  int Lmax = 0;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    int L = r < nrows ? seqlens[t0 + r] : 0;
+    L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
+    Lr[r] = L;
+    req[r] = r < nrows ? t2r[t0 + r] : -1;
+    uniform = uniform && (r >= nrows || req[r] == req[0]);
+    Lmax = max(Lmax, L);
+  }
+  const int p_begin = chunk * kPagesPerBlock;
+  if (p_begin * kPage >= Lmax) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+
+  for (int i = threadIdx.x; i < kRows * kHeads * 8; i += 256) {
+    const int r = i >> 9, h = (i >> 3) & 63, piece = i & 7;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < nrows)
+      v = *reinterpret_cast<const uint4*>(q + (t0 + r) * kQRowBytes + h * kDim + piece * 16);
+    *reinterpret_cast<uint4*>(sq + r * kQRowBytes + q_lds(h, piece)) = v;
+  }
+  for (int i = threadIdx.x; i < kRows * kHeads; i += 256)
+    sw[i] = (i >> 6) < nrows ? w[(t0 + (i >> 6)) * kHeads + (i & 63)] : 0.0f;
+  {
+    uint4* z = reinterpret_cast<uint4*>(lhist);
+    for (int i = threadIdx.x; i < kRows * kKeyBins / 8; i += 256) z[i] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  const int npass = uniform ? 1 : nrows;
+  for (int pass = 0; pass < npass; ++pass) {
+    // rows scored in this pass (bit r = row t0 + r) and their request
+    const uint32_t live = uniform ? (1u << nrows) - 1 : 1u << pass;
+    const int L = uniform ? Lmax : Lr[pass];
+    const int npages = (L + kPage - 1) / kPage;
+    if (p_begin >= npages) continue;
+    const int p_end = min(p_begin + kPagesPerBlock, npages);
+    const int32_t* prow = rpt + (int64_t)req[uniform ? 0 : pass] * rpt_stride;
+
+    const int first = p_begin + wave;
+    const int np_w = first < p_end ? (p_end - first + kWaves - 1) / kWaves : 0;
+    const int id_lane = lane < np_w ? prow[first + kWaves * lane] : -1;
+
+    auto page_id = [&](int i) -> int {   // -1: absent or invalid
+      const int id = __builtin_amdgcn_readlane(id_lane, i);
+      return (id >= 0 && id < num_pages) ? id : -1;
+    };
+    auto fetch = [&](PageKeys& pk, int i) {
+      const int id = page_id(i);
+      load_page(pk, cache + (int64_t)(id >= 0 ? id : 0) * kPageBytesFp8, c, g, lane);
+    };
+    // the 16 (row, head tile) steps of a page run as a software pipeline:
+    // the 4 MFMAs of step k+1 are issued before the ReLU-weight FMAs of
+    // step k, so the matrix core works while the vector unit reduces
+    auto mfma4 = [&](f32x4 (&acc)[4], const PageKeys& pk, int k) {
+      const int r = k >> 2, ht = k & 3;
+      const uint8_t* qr = sq + r * kQRowBytes;
+      const int h = ht * 16 + c;
+      const uint4 lo = *reinterpret_cast<const uint4*>(qr + q_lds(h, g));
+      const uint4 hi = *reinterpret_cast<const uint4*>(qr + q_lds(h, 4 + g));
+      const i32x8 qa = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            qa, pk.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    };
+    auto score = [&](const PageKeys& pk, int i) {
+      // q and the weights are re-read from LDS for every page: without this
+      // barrier the compiler hoists all four rows' operands into registers
+      // (over 300 of them) and the kernel drops to one wave per SIMD
+      asm volatile("" ::: "memory");
+      const bool b0 = g & 1, b1 = (g >> 1) & 1;
+      float res[kRows];
+      float v[4];
+      f32x4 accA[4], accB[4];
+      mfma4(accA, pk, 0);
+#pragma unroll
+      for (int k = 0; k < kRows * 4; ++k) {
+        f32x4 (&cur)[4] = (k & 1) ? accB : accA;
+        f32x4 (&nxt)[4] = (k & 1) ? accA : accB;
+        if (k + 1 < kRows * 4) mfma4(nxt, pk, k + 1);
+        const int r = k >> 2, ht = k & 3;
+        const float4 wv = *reinterpret_cast<const float4*>(sw + r * kHeads + ht * 16 + 4 * g);
+        const float wr[4] = {wv.x, wv.y, wv.z, wv.w};
+        if (ht == 0) v[0] = v[1] = v[2] = v[3] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[j] = fmaf(wr[e], relu(cur[j][e]), v[j]);
+        if (ht == 3) {
+          const float u0 = (b0 ? v[1] : v[0]) + __shfl_xor(b0 ? v[0] : v[1], 16);
+          const float u1 = (b0 ? v[3] : v[2]) + __shfl_xor(b0 ? v[2] : v[3], 16);
+          res[r] = (b1 ? u1 : u0) + __shfl_xor(b1 ? u0 : u1, 32);
+        }
+      }
+      const bool page_ok = page_id(i) >= 0;
+      const int s = (first + kWaves * i) * kPage + lane;   // position of token `lane`
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const float result = page_ok ? res[r] * pk.ks : -INFINITY;
+        if (((live >> r) & 1) && i < np_w && s < Lr[r]) {
+          logits[(t0 + r) * logits_stride + s] = result;
+          const uint32_t bin = order_key(result) >> 20;
+          atomicAdd(&lhist[r * (kKeyBins / 2) + (bin >> 1)], (bin & 1) ? 0x10000u : 1u);
+        }
+      }
+    };
+
+    if (np_w > 0) {
+      PageKeys b0, b1;
+      fetch(b0, 0);
+      for (int i = 0; i < np_w; i += 2) {
+        fetch(b1, i + 1);
+        score(b0, i);
+        fetch(b0, i + 2);
+        score(b1, i + 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kRows * kKeyBins / 2; i += 256) {
+    const int r = i / (kKeyBins / 2), b = 2 * (i % (kKeyBins / 2));
+    const uint32_t v = lhist[i];
+    if (r < nrows && v) {
+      uint32_t* dst = key_hist + (t0 + r) * kKeyBins + b;
+      if (v & 0xFFFFu) atomicAdd(dst, v & 0xFFFFu);
+      if (v >> 16) atomicAdd(dst + 1, v >> 16);
     }
   }
 }
@@ -270,6 +456,8 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
   NSA_REQUIRE(key_hist == nullptr || fp8, NSA_ERR_UNSUPPORTED,
               "%s: the fused histogram needs the fp8 path", fn);
   if (T == 0 || max_seqlen_k == 0) return nsa::ok();
+  NSA_REQUIRE(!fp8 || num_pages >= 1, NSA_ERR_INVALID_ARG,
+              "%s: empty index-key cache (num_pages 0)", fn);
   NSA_REQUIRE(q && weights && k_index_cache && real_page_table && token_to_req &&
                   seqlens_expanded && logits,
               NSA_ERR_INVALID_ARG, "%s: null pointer", fn);
@@ -286,6 +474,17 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
   if (fp8) {
     // odd, so that consecutive rows (row groups) start on different XCDs
     const int chunks = (int)((ncols + kPagesPerBlock - 1) / kPagesPerBlock) | 1;
+    if (key_hist && rows_per_request >= kRows) {
+      const int64_t blocks = (int64_t)((T + kRows - 1) / kRows) * chunks;
+      NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+      hipLaunchKernelGGL(indexer_fp8_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                         static_cast<const uint8_t*>(q), weights,
+                         static_cast<const uint8_t*>(k_index_cache), num_pages,
+                         real_page_table, rpt_stride, token_to_req,
+                         seqlens_expanded, max_seqlen_k, (int64_t)T, logits,
+                         logits_stride, chunks, key_hist);
+      return nsa::check_launch(fn);
+    }
     const int group = (rows_per_request > 1 && T % rows_per_request == 0) ? rows_per_request : 1;
     const int64_t npairs = (int64_t)(T / group) * chunks;
     const int64_t blocks = (npairs + 7) / 8 * 8 * group;

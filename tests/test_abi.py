@@ -84,6 +84,13 @@ def test_indexer_rejects_bad_arguments(lib):
     # misaligned q
     assert lib.nsa_indexer_logits(ctypes.c_void_p(257), 2, p, p, 2, 10, p, 4, p,
                                   p, 4, 64, 128, 64, 200, p, 256, N) == -1
+    # the fp8 path reads page 0 in place of an absent page: an empty cache
+    # is rejected (also with the row-group hint)
+    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 0, p, 4, p, p, 4, 64, 128, 64,
+                                  200, p, 256, N) == -1
+    assert "num_pages" in _err(lib)
+    assert lib.nsa_indexer_logits_hist(p, 2, p, p, 2, 0, p, 4, p, p, 4, 64, 128, 64,
+                                       200, p, 256, p, 4, N) == -1
 
 
 def test_topk_and_transform_reject_bad_arguments(lib):

@@ -23,7 +23,7 @@ def run_path(nsa, w, fused=True, hist=False):
                                     md["real_page_table"], md["token_to_req"],
                                     md["seqlens_expanded"], w.max_seqlen_k,
                                     dtype=idx_dtype(nsa, w), key_hist=kh,
-                                    rows_per_request=max(w.draft, 1))
+                                    rows_per_request=w.rows_per_request)
     logical = nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                      w.max_seqlen_k, key_hist=kh)
     if hist:
@@ -127,17 +127,21 @@ def _host_key_hist(logits_row, n):
     return np.bincount(key >> 20, minlength=4096)
 
 
-@pytest.mark.parametrize("name", ["decode_b32", "verify"])
-def test_fused_histogram_exact_and_topk_identical(name):
+@pytest.mark.parametrize("name,grouped", [("decode_b32", False), ("verify", False),
+                                          ("verify", True), ("extend", True)])
+def test_fused_histogram_exact_and_topk_identical(name, grouped):
+    # grouped: the rows-per-request hint of the workload, which scores a
+    # request's rows four at a time (verify: its 4 drafts; extend)
     nsa = need_gpu()
     w = full_workload(name)
-    note(f"fused histogram {name}: T={w.num_rows}")
+    note(f"fused histogram {name}: T={w.num_rows} grouped={grouped}")
     md = gpu_metadata(nsa, w)
     kh = nsa.new_key_hist(w.num_rows, DEV)
     logits = nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
                                     md["real_page_table"], md["token_to_req"],
                                     md["seqlens_expanded"], w.max_seqlen_k,
-                                    dtype=idx_dtype(nsa, w), key_hist=kh)
+                                    dtype=idx_dtype(nsa, w), key_hist=kh,
+                                    rows_per_request=w.rows_per_request if grouped else 1)
     torch.cuda.synchronize()
     L = md["seqlens_expanded"].cpu().numpy()
     hist = kh.cpu().numpy().view(np.uint32)
@@ -164,16 +168,20 @@ def test_fused_histogram_exact_and_topk_identical(name):
     ("verify", dict(bs=6, seqlen_range=(3000, 40000))),
     ("draft_extend_v2", dict(bs=5, seqlen_range=(3000, 40000))),
     ("decode_b32", dict(bs=7)),
+    # groups of 4 rows that straddle requests (extend lens not multiples of 4)
+    ("extend", dict(bs=3, extend_lens=[5, 130, 63], prefix_lens=[100, 3000, 777])),
+    ("draft_extend", dict(bs=9, seqlen_range=(100, 9000))),
 ])
 def test_indexer_row_groups_change_nothing(name, overrides):
-    # grouping the rows of a request only reorders the blocks: logits and
-    # histogram counts are identical (ungrouped, grouped, and a group size
-    # that does not match the layout)
+    # the row-group hint changes the schedule (XCD-adjacent blocks for 2 or
+    # 3, four rows per block sharing their key pages for 4 and more), never
+    # the result: logits, unwritten positions and histogram counts are
+    # identical for every hint, including ones that do not match the layout
     nsa = need_gpu()
     w = W.make_workload(name, device=DEV, parts=("indexer",), **overrides)
     md = gpu_metadata(nsa, w)
     outs = []
-    for g in (1, max(w.draft, 1), 3):
+    for g in (1, 2, 3, 4, 8, max(w.draft, 1)):
         kh = nsa.new_key_hist(w.num_rows, DEV)
         lg = torch.full((w.num_rows, nsa.logits_row_stride(w.max_seqlen_k)), 7.0,
                         device=DEV)
@@ -185,3 +193,30 @@ def test_indexer_row_groups_change_nothing(name, overrides):
         outs.append((lg.cpu(), kh.cpu()))
     for lg, kh in outs[1:]:
         assert torch.equal(lg, outs[0][0]) and torch.equal(kh, outs[0][1])
+
+
+def test_indexer_row_groups_with_unordered_rows():
+    # rows whose requests are not consecutive (a caller-built token_to_req):
+    # groups of four then mix requests and are scored row by row; the result
+    # equals the one-row schedule's bit for bit
+    nsa = need_gpu()
+    w = W.make_workload("verify", device=DEV, parts=("indexer",), bs=6,
+                        seqlen_range=(200, 20000))
+    md = gpu_metadata(nsa, w)
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(w.num_rows, generator=g).to(DEV)
+    t2r = md["token_to_req"][perm].contiguous()
+    lens = md["seqlens_expanded"][perm].contiguous()
+    lens[3] = 0                                   # an empty row
+    outs = []
+    for hint in (1, 4):
+        kh = nsa.new_key_hist(w.num_rows, DEV)
+        lg = torch.full((w.num_rows, nsa.logits_row_stride(w.max_seqlen_k)), 7.0,
+                        device=DEV)
+        nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
+                               md["real_page_table"], t2r, lens, w.max_seqlen_k,
+                               logits=lg, key_hist=kh, rows_per_request=hint)
+        torch.cuda.synchronize()
+        outs.append((lg.cpu(), kh.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert int(outs[1][1][3].sum()) == 0 and bool((outs[1][0][3] == 7.0).all())

@@ -107,6 +107,12 @@ class Workload:
     kv_bf16: torch.Tensor = None      # [num_pages * 64, 576] bf16
     host: dict = field(default_factory=dict)
 
+    @property
+    def rows_per_request(self):
+        """Mean query rows per request, rounded down: the indexer's hint
+        for letting a request's rows share their key-page reads."""
+        return max(self.num_rows // self.bs, 1) if self.bs else 1
+
 
 def _randint(gen, lo, hi, n, device):
     return torch.randint(lo, hi + 1, (n,), generator=gen, device=device,
