@@ -210,7 +210,7 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
 
 // Rows that share a request (target-verify, draft-extend v2, extend) read the
 // same key pages. This kernel scores each page once for kRows consecutive
-// rows: a block takes (group of kRows rows, chunk of 32 pages) and every
+// rows: a block takes (group of kRows rows, chunk of 64 pages) and every
 // wave scores its page buffer against all rows of the group, so the key
 // bytes read per row drop kRows-fold and MFMA work per byte rises as much.
 // q (8 KB per row) and the head weights of the group sit in LDS instead of
@@ -222,6 +222,10 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
 // serves the histogram entry point only.
 constexpr int kRows = 4;
 constexpr int kQRowBytes = kHeads * kDim;  // 8192
+// 64 pages per block (16 per wave): the per-block costs (staging q, clearing
+// and flushing four histograms) are spread over twice the MFMA work of the
+// one-row kernel's 32; a row's count per bin stays below 2^16 (4096 keys)
+constexpr int kRowsPagesPerBlock = 64;
 
 // LDS offset of 16-byte piece `piece` of head h's q row: pieces are rotated by
 // (h >> 1) & 7, so the 16 lanes of one ds_read_b128 (heads c = 0..15 of a
@@ -241,7 +245,7 @@ indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__
                         uint32_t* __restrict__ key_hist) {
   __shared__ __align__(16) uint8_t sq[kRows * kQRowBytes];
   __shared__ __align__(16) float sw[kRows * kHeads];
-  // two 16-bit counts per word: a block writes at most 2048 logits per row
+  // two 16-bit counts per word: a block writes at most 4096 logits per row
   __shared__ __align__(16) uint32_t lhist[kRows * kKeyBins / 2];
 
   const int64_t t0 = (int64_t)(blockIdx.x / chunks_per_group) * kRows;
@@ -260,7 +264,7 @@ indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__
     uniform = uniform && (r >= nrows || req[r] == req[0]);
     Lmax = max(Lmax, L);
   }
-  const int p_begin = chunk * kPagesPerBlock;
+  const int p_begin = chunk * kRowsPagesPerBlock;
   if (p_begin * kPage >= Lmax) return;
 
   const int lane = threadIdx.x & 63;
@@ -289,7 +293,7 @@ indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__
     const int L = uniform ? Lmax : Lr[pass];
     const int npages = (L + kPage - 1) / kPage;
     if (p_begin >= npages) continue;
-    const int p_end = min(p_begin + kPagesPerBlock, npages);
+    const int p_end = min(p_begin + kRowsPagesPerBlock, npages);
     const int32_t* prow = rpt + (int64_t)req[uniform ? 0 : pass] * rpt_stride;
 
     const int first = p_begin + wave;
@@ -374,13 +378,17 @@ indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kRows * kKeyBins / 2; i += 256) {
-    const int r = i / (kKeyBins / 2), b = 2 * (i % (kKeyBins / 2));
-    const uint32_t v = lhist[i];
-    if (r < nrows && v) {
-      uint32_t* dst = key_hist + (t0 + r) * kKeyBins + b;
-      if (v & 0xFFFFu) atomicAdd(dst, v & 0xFFFFu);
-      if (v >> 16) atomicAdd(dst + 1, v >> 16);
+  // 16 bytes (8 bins) per thread and step; rows past the group's end skipped
+  for (int i = threadIdx.x; i < nrows * kKeyBins / 8; i += 256) {
+    const uint4 v4 = reinterpret_cast<const uint4*>(lhist)[i];
+    if ((v4.x | v4.y | v4.z | v4.w) == 0) continue;
+    const int r = i / (kKeyBins / 8), b = 8 * (i % (kKeyBins / 8));
+    uint32_t* dst = key_hist + (t0 + r) * kKeyBins + b;
+    const uint32_t v[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (v[e] & 0xFFFFu) atomicAdd(dst + 2 * e, v[e] & 0xFFFFu);
+      if (v[e] >> 16) atomicAdd(dst + 2 * e + 1, v[e] >> 16);
     }
   }
 }
@@ -475,14 +483,15 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
     // odd, so that consecutive rows (row groups) start on different XCDs
     const int chunks = (int)((ncols + kPagesPerBlock - 1) / kPagesPerBlock) | 1;
     if (key_hist && rows_per_request >= kRows) {
-      const int64_t blocks = (int64_t)((T + kRows - 1) / kRows) * chunks;
+      const int rchunks = (int)((ncols + kRowsPagesPerBlock - 1) / kRowsPagesPerBlock) | 1;
+      const int64_t blocks = (int64_t)((T + kRows - 1) / kRows) * rchunks;
       NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
       hipLaunchKernelGGL(indexer_fp8_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                          static_cast<const uint8_t*>(q), weights,
                          static_cast<const uint8_t*>(k_index_cache), num_pages,
                          real_page_table, rpt_stride, token_to_req,
                          seqlens_expanded, max_seqlen_k, (int64_t)T, logits,
-                         logits_stride, chunks, key_hist);
+                         logits_stride, rchunks, key_hist);
       return nsa::check_launch(fn);
     }
     const int group = (rows_per_request > 1 && T % rows_per_request == 0) ? rows_per_request : 1;
