@@ -9,7 +9,8 @@
 //   logits[t, s] = kscale[s] * sum_h w[t, h] * relu(q[t, h, :] . k[s, :]).
 //
 // fp8 path (Hi = 64 heads, Di = 128), MI355X design:
-//   * one block of 4 waves per (row, chunk of 32 pages), in plain row-major
+//   * one block of 4 waves per (row, chunk of 32 pages; 16 or 8 for a batch
+//     too small to give 1024 blocks), in plain row-major
 //     order with the chunk count per row padded to an odd number: work groups
 //     are dealt to the 8 XCDs round-robin, so a row's chunks start on a
 //     different XCD than the previous row's and rows of unequal length
@@ -48,7 +49,10 @@ constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kPageBytesFp8 = kPage * kDim + kPage * 4;  // 8448
 constexpr int kWaves = 4;
+// pages per block of the one-row kernel: 32, or 16 / 8 when that leaves
+// fewer than kMinBlocks blocks (a small batch would not fill the CUs)
 constexpr int kPagesPerBlock = 32;
+constexpr int64_t kMinBlocks = 1024;
 
 struct PageKeys {
   i32x8 k[4];  // 4 tiles of 16 tokens
@@ -91,8 +95,8 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    const int32_t* __restrict__ t2r,
                    const int32_t* __restrict__ seqlens, int max_seqlen_k,
                    float* __restrict__ logits, int64_t logits_stride,
-                   int chunks_per_row, int group, int64_t npairs,
-                   uint32_t* __restrict__ key_hist) {
+                   int chunks_per_row, int pages_per_block, int group,
+                   int64_t npairs, uint32_t* __restrict__ key_hist) {
   __shared__ uint32_t lhist[HIST ? kKeyBins : 1];
   // block -> (row group, chunk) pair qi and row j of the group: the blocks
   // of one pair are `group` consecutive slots of one XCD's sequence (for
@@ -105,9 +109,9 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
   int L = seqlens[t];
   L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
   const int npages = (L + kPage - 1) / kPage;
-  const int p_begin = chunk * kPagesPerBlock;
+  const int p_begin = chunk * pages_per_block;
   if (p_begin >= npages) return;
-  const int p_end = min(p_begin + kPagesPerBlock, npages);
+  const int p_end = min(p_begin + pages_per_block, npages);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -495,7 +499,13 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
       return nsa::check_launch(fn);
     }
     const int group = (rows_per_request > 1 && T % rows_per_request == 0) ? rows_per_request : 1;
-    const int64_t npairs = (int64_t)(T / group) * chunks;
+    int ppb = kPagesPerBlock;
+    int chunks_ppb = chunks;
+    while (ppb > 8 && (int64_t)T * chunks_ppb < kMinBlocks) {
+      ppb /= 2;
+      chunks_ppb = (int)((ncols + ppb - 1) / ppb) | 1;
+    }
+    const int64_t npairs = (int64_t)(T / group) * chunks_ppb;
     const int64_t blocks = (npairs + 7) / 8 * 8 * group;
     NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
     auto kern = key_hist ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>;
@@ -504,7 +514,7 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
                        static_cast<const uint8_t*>(k_index_cache), num_pages,
                        real_page_table, rpt_stride, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits, logits_stride,
-                       chunks, group, npairs, key_hist);
+                       chunks_ppb, ppb, group, npairs, key_hist);
   } else {
     const int chunks = (max_seqlen_k + 255) / 256;
     const int64_t blocks = (int64_t)T * chunks;
