@@ -321,8 +321,17 @@ topk_hist_kernel(const float* __restrict__ logits, int64_t logits_stride,
 // GIVEN: the row histograms come from the indexer (key_hist, [T][4096]
 // uint32) instead of pass 1; each row of key_hist is cleared once read, and a
 // row whose counts do not add up to its length takes the multi-pass select.
-template <bool VEC, bool GIVEN>
-__global__ void __launch_bounds__(kThreads)
+// SMALL: batches of at least kSmallMinRows rows of at most kSmallMapBits
+// positions (max_seqlen_k bounds them), such as chunked extend. An 8 KB
+// bitmap, a 4096-entry candidate store and a 2048-bin radix histogram take
+// 48 KB of LDS instead of 144, and the kernel keeps to 64 VGPRs, so two
+// blocks share a CU and their row passes and barriers overlap. With fewer
+// rows than CUs there is nothing to overlap and the smaller register budget
+// only costs time, hence the row minimum.
+constexpr int kSmallMapBits = 65536;
+constexpr int kSmallMinRows = 512;
+template <bool VEC, bool GIVEN, bool SMALL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SMALL ? 8 : 1)))
 topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
                    const int32_t* __restrict__ lengths, int topk,
                    int max_seqlen_k, int chunks,
@@ -331,10 +340,14 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
                    const int32_t* __restrict__ table, int64_t table_stride,
                    const int32_t* __restrict__ t2r, int32_t* __restrict__ out,
                    int64_t out_stride) {
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t bitmap[kMapWords];
-  __shared__ uint32_t cand_key[kCap];
-  __shared__ int32_t cand_pos[kCap];
+  constexpr int kMB = SMALL ? kSmallMapBits : kMapBits;   // bitmap bits
+  constexpr int kMW = kMB / 32;
+  constexpr int kCP = SMALL ? 4096 : kCap;                 // candidate store
+  static_assert(kCP >= kMapBits / NSA_PAGE_SIZE, "page table fits the candidate store");
+  __shared__ uint32_t hist[SMALL ? 2048 : kHistBins];     // radix passes use <= 2048 bins
+  __shared__ uint32_t bitmap[kMW];
+  __shared__ uint32_t cand_key[kCP];
+  __shared__ int32_t cand_pos[kCP];
   __shared__ int scan_buf[2 * kWaves + 1];
   __shared__ uint32_t s_sel[4];
   __shared__ int s_ncand;
@@ -401,7 +414,7 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
     return;
   }
   const int nw = (n + 31) >> 5;
-  if (n <= kMapBits)
+  if (n <= kMB)
     for (int w = tid; w < nw; w += kThreads) bitmap[w] = 0u;
   if (tid == 0) s_ncand = 0;
   publish_threshold<4>(hc, (uint32_t)(tot - hex) - hs, topk, s_sel);
@@ -411,7 +424,7 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   bool exact = s_sel[2] != 0;
   const uint32_t cnt_b = s_sel[3];
   __syncthreads();
-  if (cnt_b > (uint32_t)kCap || n > kMapBits) {
+  if (cnt_b > (uint32_t)kCP || n > kMB) {
     select_multipass(row, n, VEC, topk, orow, map, hist, scan_buf, s_sel);
     return;
   }
@@ -461,7 +474,7 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
         }
         const uint32_t w = or_lanes8(m << ((tid & 7) * 4));
         const int word = pos >> 5;
-        if ((tid & 7) == 0 && word < kMapWords) bitmap[word] = w;
+        if ((tid & 7) == 0 && word < kMW) bitmap[word] = w;
       }
       // a lane with candidates reserves its slots with one LDS atomic (the
       // order of the candidates does not matter to the exact selection)
@@ -470,7 +483,7 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
       while (cm) {
         const int b = __ffs(cm) - 1;
         cm &= cm - 1;
-        if (q < kCap) cand_pos[q] = b0 + (b >> 2) * kSpan + tid * 4 + (b & 3);
+        if (q < kCP) cand_pos[q] = b0 + (b >> 2) * kSpan + tid * 4 + (b & 3);
         ++q;
       }
     };
@@ -492,11 +505,11 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
       atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
     } else if ((k >> 20) == bin) {
       const int q = atomicAdd(&s_ncand, 1);
-      if (q < kCap) cand_pos[q] = pos;
+      if (q < kCP) cand_pos[q] = pos;
     }
   }
   __syncthreads();
-  const int nc = min(s_ncand, kCap);
+  const int nc = min(s_ncand, kCP);
   // keys of the candidates, read back from the row (just read, so cached)
   for (int i = tid; i < nc; i += kThreads) cand_key[i] = order_key(row[cand_pos[i]]);
   // the row's page-table entries for the output, loaded now (branch-free:
@@ -568,8 +581,8 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
     if (keep) atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
   }
   __syncthreads();
-  int32_t* ptab = reinterpret_cast<int32_t*>(cand_key);   // kCap >= 4096 entries
-  static_assert(kCap >= kTabPer * kThreads, "page table fits the candidate store");
+  int32_t* ptab = reinterpret_cast<int32_t*>(cand_key);   // >= 4096 entries
+  static_assert(kCP >= kTabPer * kThreads, "page table fits the candidate store");
   if (trow) {
 #pragma unroll
     for (int k = 0; k < kTabPer; ++k) ptab[tid + k * kThreads] = tab[k];
@@ -658,7 +671,9 @@ extern "C" int nsa_topk_transform(const float* logits, int64_t logits_stride,
     int st = nsa::check_launch(fn);
     if (st != NSA_OK) return st;
   }
-  auto sel = vec ? topk_select_kernel<true, false> : topk_select_kernel<false, false>;
+  const bool small = max_seqlen_k <= kSmallMapBits && T >= kSmallMinRows;
+  auto sel = vec ? (small ? topk_select_kernel<true, false, true> : topk_select_kernel<true, false, false>)
+                 : (small ? topk_select_kernel<false, false, true> : topk_select_kernel<false, false, false>);
   hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, s, logits, logits_stride,
                      lengths, topk, max_seqlen_k, chunks, ws, nullptr, table,
                      table_stride, token_to_req, out, out_stride);
@@ -695,7 +710,9 @@ extern "C" int nsa_topk_transform_hist(const float* logits, int64_t logits_strid
                 "%s: table_stride < ceil(max_seqlen_k/64)", fn);
   }
   const bool vec = logits && nsa::aligned(logits, 16) && logits_stride % 4 == 0;
-  auto sel = vec ? topk_select_kernel<true, true> : topk_select_kernel<false, true>;
+  const bool small = max_seqlen_k <= kSmallMapBits && T >= kSmallMinRows;
+  auto sel = vec ? (small ? topk_select_kernel<true, true, true> : topk_select_kernel<true, true, false>)
+                 : (small ? topk_select_kernel<false, true, true> : topk_select_kernel<false, true, false>);
   hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, (hipStream_t)stream,
                      logits, logits_stride, lengths, topk, max_seqlen_k, 0,
                      nullptr, key_hist, table, table_stride, token_to_req, out,

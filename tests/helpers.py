@@ -161,3 +161,15 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, kind, what=""):
 def full_workload(name):
     """Full-size workload generated on the GPU (cached for the session)."""
     return W.make_workload(name, device=DEV, seed=0)
+
+
+def host_key_hist(logits_row, n):
+    """Histogram of the top 12 bits of the order-preserving key (NaN lowest,
+    -0 == +0) over positions [0, n): the definition stated in nsa.h."""
+    x = np.ascontiguousarray(logits_row[:n], dtype=np.float32)
+    u = x.view(np.uint32).copy()
+    u[x == 0] = 0
+    neg = (u & 0x80000000) != 0
+    key = np.where(neg, ~u, u | 0x80000000).astype(np.uint32)
+    key[np.isnan(x)] = 0
+    return np.bincount(key >> 20, minlength=4096)

@@ -11,7 +11,7 @@ import workloads as W
 import oracle
 from helpers import (DEV, need_gpu, note, to_dev, oracle_metadata, gpu_metadata,
                      idx_dtype, oracle_logits_rows, check_logits, check_topk_row,
-                     oracle_kv_rows, check_attention, full_workload)
+                     oracle_kv_rows, check_attention, full_workload, host_key_hist)
 
 pytestmark = pytest.mark.gpu
 
@@ -115,18 +115,6 @@ def test_pipeline_full_size_sampled(name):
     check_rows(w, *res, rows=rows)
 
 
-def _host_key_hist(logits_row, n):
-    """Histogram of the top 12 bits of the order-preserving key (NaN lowest,
-    -0 == +0) over positions [0, n): the definition stated in nsa.h."""
-    x = np.ascontiguousarray(logits_row[:n], dtype=np.float32)
-    u = x.view(np.uint32).copy()
-    u[x == 0] = 0
-    neg = (u & 0x80000000) != 0
-    key = np.where(neg, ~u, u | 0x80000000).astype(np.uint32)
-    key[np.isnan(x)] = 0
-    return np.bincount(key >> 20, minlength=4096)
-
-
 @pytest.mark.parametrize("name,grouped", [("decode_b32", False), ("verify", False),
                                           ("verify", True), ("extend", True)])
 def test_fused_histogram_exact_and_topk_identical(name, grouped):
@@ -147,7 +135,7 @@ def test_fused_histogram_exact_and_topk_identical(name, grouped):
     hist = kh.cpu().numpy().view(np.uint32)
     for t in sorted({0, int(np.argmax(L)), int(np.argmin(L)), w.num_rows - 1}):
         n = min(int(L[t]), w.max_seqlen_k)
-        np.testing.assert_array_equal(hist[t], _host_key_hist(logits[t].cpu().numpy(), n),
+        np.testing.assert_array_equal(hist[t], host_key_hist(logits[t].cpu().numpy(), n),
                                       err_msg=f"{name} row {t}")
     assert (hist.sum(axis=1) == np.minimum(L, w.max_seqlen_k)).all()
     args = (logits, md["seqlens_expanded"], w.topk, w.max_seqlen_k)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from helpers import (DEV, need_gpu, note, check_topk_row, check_attention,
-                     CacheFromRows)
+                     CacheFromRows, host_key_hist)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,25 +42,86 @@ def _topk_rows(rng, lengths, width, kind):
     return x
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "const", "special", "neg_inf_heavy",
-                                  "pos_inf_heavy"])
+KINDS = ["normal", "ties", "const", "special", "neg_inf_heavy", "pos_inf_heavy"]
+# row lengths around the edges of the select: rows of at most topk, the
+# 16384-position histogram chunks, 1..3 positions past the last vector; the
+# "short" set keeps the row width (max_seqlen_k) within 65536 positions and
+# is repeated to 516 rows (the select's short-row variant, used for batches of
+# at least 512 such rows); repeated rows must equal their first copy
+LENGTHS = {
+    "long": lambda k: [0, 1, k - 1, k, k + 1, 3 * k + 5, 20000, 131072 - 3,
+                       16384, 16385, 32768 + 11],
+    "short": lambda k: [0, 1, k - 1, k, k + 1, 3 * k + 5, 20000, 65536 - 131,
+                        16384, 16385, 32768 + 11, 65536 - 192],
+}
+SHORT_ROWS = 516
+
+
+def _tile_rows(x, lengths, span):
+    if span != "short":
+        return x, lengths
+    reps = -(-SHORT_ROWS // len(lengths))
+    return np.tile(x, (reps, 1))[:SHORT_ROWS], (lengths * reps)[:SHORT_ROWS]
+
+
+def _check_repeats(got, n0):
+    for t in range(n0, len(got)):
+        np.testing.assert_array_equal(got[t], got[t % n0], err_msg=f"repeated row {t}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("topk", [256, 2048])
 @pytest.mark.parametrize("pad", [6, 67])   # odd row stride: scalar loads; else vector
-def test_topk_exact_on_given_logits(kind, topk, pad):
+@pytest.mark.parametrize("span", ["long", "short"])
+def test_topk_exact_on_given_logits(kind, topk, pad, span):
     nsa = need_gpu()
-    note(f"topk exact {kind} topk={topk} pad={pad}")
+    note(f"topk exact {kind} topk={topk} pad={pad} {span}")
     rng = np.random.default_rng(topk)
-    lengths = [0, 1, topk - 1, topk, topk + 1, 3 * topk + 5, 20000, 131072 - 3,
-               16384, 16385, 32768 + 11]
+    lengths = LENGTHS[span](topk)
+    n0 = len(lengths)
     width = max(lengths) + pad
     x = _topk_rows(rng, lengths, width, kind)
-    lg = torch.as_tensor(x, device=DEV)
-    ln = torch.as_tensor(lengths, dtype=torch.int32, device=DEV)
+    xt, lt = _tile_rows(x, lengths, span)
+    lg = torch.as_tensor(xt, device=DEV)
+    ln = torch.as_tensor(lt, dtype=torch.int32, device=DEV)
     got = nsa.nsa_topk_transform(lg, ln, topk, width).cpu().numpy()
+    _check_repeats(got, n0)
     for t, L in enumerate(lengths):
         sel = got[t]
         check_topk_row(sel, L, topk, what=f"row {t}")
         # both sides break ties by position and rank NaN lowest: equal sets
+        want = oracle.topk.topk_row(x[t].astype(np.float64), L, topk)
+        want = np.sort(want[want >= 0])
+        np.testing.assert_array_equal(sel[:len(want)], want, err_msg=f"row {t} L={L}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("pad", [6, 67])
+@pytest.mark.parametrize("span", ["long", "short"])
+def test_topk_with_histogram_exact_on_given_logits(kind, pad, span):
+    # the select that takes the indexer's row histograms (here the histogram
+    # of the same logits, computed on the host from its definition): each
+    # row equals the oracle's set, and the histogram is left zero
+    nsa = need_gpu()
+    topk = 2048
+    note(f"topk with histogram {kind} pad={pad} {span}")
+    rng = np.random.default_rng(7)
+    lengths = LENGTHS[span](topk)
+    n0 = len(lengths)
+    width = max(lengths) + pad
+    x = _topk_rows(rng, lengths, width, kind)
+    kh_host = np.stack([host_key_hist(x[t], L) for t, L in enumerate(lengths)])
+    xt, lt = _tile_rows(x, lengths, span)
+    kh_host, _ = _tile_rows(kh_host, lengths, span)
+    kh = torch.as_tensor(kh_host.astype(np.uint32).view(np.int32), device=DEV)
+    lg = torch.as_tensor(xt, device=DEV)
+    ln = torch.as_tensor(lt, dtype=torch.int32, device=DEV)
+    got = nsa.nsa_topk_transform(lg, ln, topk, width, key_hist=kh).cpu().numpy()
+    assert int(kh.abs().sum()) == 0
+    _check_repeats(got, n0)
+    for t, L in enumerate(lengths):
+        sel = got[t]
+        check_topk_row(sel, L, topk, what=f"row {t}")
         want = oracle.topk.topk_row(x[t].astype(np.float64), L, topk)
         want = np.sort(want[want >= 0])
         np.testing.assert_array_equal(sel[:len(want)], want, err_msg=f"row {t} L={L}")
