@@ -177,9 +177,10 @@ def cpu_baseline(w, rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus "
-              f"{args.gpus}); each GPU would run its own share of requests "
-              "with no exchange)", file=sys.stderr)
+        print(f"bench.py: one GPU per process only (asked for --gpus "
+              f"{args.gpus}); decode shards over requests with no exchange, so "
+              "each GPU would run this benchmark on its own share of requests",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

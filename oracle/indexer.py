@@ -22,7 +22,7 @@ pages never show it, this formula is a reading: the tests pin this oracle's
 implementation of it (closed forms, brute force, page-order invariance), not
 the reading. Positions s >= L_t are not scored (returned as -inf here).
 
-Index-key cache page layout (a choice, listed in the design doc): each 64-token
+Index-key cache page layout (a choice): each 64-token
 page holds 64 rows of ``Di`` key elements (fp8 codes, or fp32 for the tiny
 configuration) followed by 64 little-endian fp32 per-token scales.
 """

@@ -16,7 +16,7 @@ Follows the metadata construction on the pages:
   the fixed number of draft tokens, ``seq_lens`` already counting them), and
   the v2 branch of ``init_forward_metadata_replay_cuda_graph``.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * ``compute_nsa_seqlens`` is not shown; the field comment says the result is
   the expanded seqlens "clipped to topk", read as an elementwise minimum.

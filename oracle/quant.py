@@ -5,8 +5,8 @@ The pages call ``quantize_k_cache(kv_cache)`` to turn the bf16 latent cache
 into the fp8 format the sparse decode kernel reads ("nsa_backend.py
 (EngineX-Hygon sglang fork)", ``_forward_flashmla_decode``; "dsa_backend.py
 (sglang main)", ``_forward_flashmla_kv``), viewed as ``[pages, 64, 1,
-kv_cache_dim]``. Its body is not shown. Reading adopted (listed in the design doc),
-one 656-byte row per slot:
+kv_cache_dim]``. Its body is not shown. Reading adopted, one 656-byte row
+per slot:
 
     bytes   0..511  e4m3fn codes of the 512 no-rope values, in 4 blocks of 128
     bytes 512..527  4 little-endian fp32 block scales

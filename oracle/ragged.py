@@ -21,7 +21,7 @@ attention reads a contiguous bf16 copy of the batch's latent rows.
   entries of an index matrix, ``kv_indptr[1:] = cumsum(count of != -1 per
   row)`` and the valid entries of every row, in order, concatenated.
 
-Readings (listed in the design doc): the body of ``dequantize_k_cache_paged`` is
+Readings: the body of ``dequantize_k_cache_paged`` is
 not shown; each value is read as the fp32 product of its e4m3 code and block
 scale rounded to bf16 (nearest even), the rope values copied, and a slot
 outside the cache giving a zero row.

@@ -1,7 +1,7 @@
 """Shared pieces of the GPU parity tests: device workloads, oracle-side views
 of the same inputs, and the acceptance checks with their tolerances.
 
-Tolerances (derivations in the design doc):
+Tolerances:
 * metadata, page transform, fp8 cache bytes: bit-exact.
 * indexer logits: |gpu - oracle| <= 1e-3 + 1e-4 * |oracle| (fp32 sums of exact
   fp8 products; the error bound is ~(128 + 64) * 2^-24 of the sum of |terms|).
