@@ -19,7 +19,7 @@ Follows the metadata construction on the pages:
 Readings where the pages are silent:
 
 * ``compute_nsa_seqlens`` is not shown; the field comment says the result is
-  the expanded seqlens "clipped to topk", read as an elementwise minimum.
+  the expanded seqlens limited to topk, read as an elementwise minimum.
 * Target-verify rows: one query row per draft token (``cu_seqlens_q`` steps by
   one, ``max_seqlen_q`` is 1), as the sglang-main page builds it.
 * Draft-extend rows: as on the sglang-main page, one query row per token

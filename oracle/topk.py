@@ -3,7 +3,7 @@
 Follows "nsa_backend.py (EngineX-Hygon sglang fork)",
 ``NSAIndexerMetadata.topk_transform``: the selection gets the logits and the
 expanded seqlens as ``lengths`` and returns ``topk`` indices per row; the
-``nsa_cache_seqlens_int32`` field comment ("clipped to topk") fixes that a row
+``nsa_cache_seqlens_int32`` field comment (its lengths are limited to topk) fixes that a row
 keeps ``min(L, topk)`` positions. Unused entries are -1, the padding value the
 pages use for index rows ("dsa_backend.py (sglang main)",
 ``_pad_topk_indices``).

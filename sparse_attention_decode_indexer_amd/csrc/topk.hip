@@ -2,7 +2,7 @@
 //
 // "nsa_backend.py (EngineX-Hygon sglang fork)", NSAIndexerMetadata.
 // topk_transform: fast_topk_v2(logits, lengths=seqlens_expanded, topk) keeps
-// at most topk positions per row ("clipped to topk", NSAMetadata); the fused
+// at most topk positions per row (NSAMetadata limits the lengths to topk); the fused
 // variant fast_topk_transform_fused returns physical slots through the page
 // table instead of logical positions.
 //
