@@ -210,3 +210,23 @@ def test_ragged_entry_points_validate(lib):
     assert lib.nsa_valid_kv_indices(p, 8, 2, 8, p, N, 16, N) == -1           # null kv_indices
     assert lib.nsa_valid_kv_indices(p, 8, -2, 8, p, p, 16, N) == -1
     assert "nsa_valid_kv_indices" in lib.nsa_last_error().decode()
+
+
+def test_empty_batches_launch_nothing(lib):
+    # no query rows (T = 0) or no slots: every compute entry point returns OK
+    # before it touches a pointer, so NULL buffers are accepted
+    P = ctypes.c_void_p
+    f = ctypes.c_float
+    assert lib.nsa_indexer_logits(N, 2, N, N, 2, 10, N, 4, N, N, 0, 64, 128, 64,
+                                  256, N, 256, N) == 0
+    assert lib.nsa_indexer_logits_hist(N, 2, N, N, 2, 10, N, 4, N, N, 0, 64, 128, 64,
+                                       256, N, 256, N, 1, N) == 0
+    assert lib.nsa_topk_transform(N, 0, N, 0, 64, 256, N, 0, N, 64, N, 64, N, 0, N) == 0
+    assert lib.nsa_topk_transform_hist(N, 0, N, 0, 64, 256, N, 0, N, 64, N, N, 64, N) == 0
+    assert lib.nsa_page_table_transform(N, 64, 0, 64, N, 0, 0, P(16), 4, 4, 64, N, N,
+                                        64, N) == 0
+    for entry in (lib.nsa_sparse_mla_decode, lib.nsa_sparse_mla_extend):
+        assert entry(N, 0, 576, N, 0, 0, N, 64, N, 0, 16, 64, 576, 512, f(0.1),
+                     N, N, N, 0, N) == 0
+    assert lib.nsa_quantize_k_cache(N, 0, 576, N, N) == 0
+    assert _err(lib) == ""

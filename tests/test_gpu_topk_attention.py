@@ -127,6 +127,37 @@ def test_topk_with_histogram_exact_on_given_logits(kind, pad, span):
         np.testing.assert_array_equal(sel[:len(want)], want, err_msg=f"row {t} L={L}")
 
 
+def test_topk_without_logits_when_rows_fit():
+    # every row holds at most topk positions (max_seqlen_k <= topk): no
+    # logits are needed; each row keeps all its positions in order, mapped
+    # through the page table, then -1 (with and without a histogram)
+    nsa = need_gpu()
+    topk, width = 256, 200
+    lengths = [0, 1, 63, 64, 65, 199, 200]
+    ln = torch.as_tensor(lengths, dtype=torch.int32, device=DEV)
+    rng = np.random.default_rng(3)
+    table = torch.as_tensor(rng.permutation(64)[:2 * 4].reshape(2, 4), dtype=torch.int32,
+                            device=DEV)
+    t2r = torch.as_tensor([i % 2 for i in range(len(lengths))], dtype=torch.int32,
+                          device=DEV)
+    logical = nsa.nsa_topk_transform(None, ln, topk, width).cpu().numpy()
+    slots = nsa.nsa_topk_transform(None, ln, topk, width, table=table,
+                                   token_to_req=t2r).cpu().numpy()
+    kh = nsa.new_key_hist(len(lengths), DEV)
+    kh[:, 7] = 5                                   # any content: cleared, unused
+    slots_h = nsa.nsa_topk_transform(None, ln, topk, width, table=table,
+                                     token_to_req=t2r, key_hist=kh).cpu().numpy()
+    assert int(kh.abs().sum()) == 0
+    tab = table.cpu().numpy()
+    for t, L in enumerate(lengths):
+        want = np.full(topk, -1, np.int64)
+        want[:L] = np.arange(L)
+        np.testing.assert_array_equal(logical[t], want)
+        want_s = np.where(want >= 0, tab[t % 2][np.maximum(want, 0) // 64] * 64 + want % 64, -1)
+        np.testing.assert_array_equal(slots[t], want_s)
+        np.testing.assert_array_equal(slots_h[t], want_s)
+
+
 def test_topk_fused_table_and_strides():
     nsa = need_gpu()
     rng = np.random.default_rng(1)
