@@ -159,6 +159,8 @@ def test_fused_histogram_exact_and_topk_identical(name, grouped):
     # groups of 4 rows that straddle requests (extend lens not multiples of 4)
     ("extend", dict(bs=3, extend_lens=[5, 130, 63], prefix_lens=[100, 3000, 777])),
     ("draft_extend", dict(bs=9, seqlen_range=(100, 9000))),
+    # full size: the one-row schedule (hint 1) ends with short tail blocks
+    ("decode_b128", {}),
 ])
 def test_indexer_row_groups_change_nothing(name, overrides):
     # the row-group hint changes the schedule (XCD-adjacent blocks for 2 or
