@@ -43,6 +43,12 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=40,
                     help="rows of the oracle sample (0 = skip the CPU leg)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single steps, each after writing a 1 GiB "
+                         "buffer so no input is left in the 256 MB last-level "
+                         "cache (cold_ms_per_step) and each without it "
+                         "(single_ms_per_step); value stays the warm, "
+                         "back-to-back rate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (a known-size "
                          "kernel for scaling HBM counters)")
@@ -261,6 +267,30 @@ def main():
 
     stage = np.array([[ev[k][i].elapsed_time(ev[k][i + 1]) for i in range(4)]
                       for k in range(args.steps)])          # ms
+    cold_ms = single_ms = None
+    if args.cold:
+        # each step timed alone (HIP events around it, synchronised); for the
+        # cold time a 1 GiB fill outside the events first evicts the inputs
+        # from the last-level cache
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+        def lone(evict):
+            times = []
+            for k in range(args.steps):
+                if evict:
+                    flush.fill_(float(k))
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                step()
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+            return float(np.median(times))
+
+        single_ms = lone(False)
+        cold_ms = lone(True)
+        del flush
     stage_ms = stage.mean(axis=0)
     ms_per_step = elapsed * 1e3 / args.steps
     se = md["seqlens_expanded"].cpu().numpy()     # visible length of every row
@@ -315,6 +345,9 @@ def main():
                       "topk_transform": stage_ms[2], "sparse_mla": stage_ms[3]},
         "cpu_baseline": None,
     }
+    if cold_ms is not None:
+        res["single_ms_per_step"] = single_ms
+        res["cold_ms_per_step"] = cold_ms
     if args.cpu_rows > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(res), flush=True)
