@@ -54,10 +54,50 @@ constexpr int kWaves = 4;
 constexpr int kPagesPerBlock = 32;
 constexpr int64_t kMinBlocks = 1024;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Orders one wave's LDS writes before its later LDS reads (and the reads
+// before later writes) for the compiler; the hardware runs a wave's LDS
+// instructions in order.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct PageKeys {
   i32x8 k[4];  // 4 tiles of 16 tokens
   float ks;    // scale of token `lane`
 };
+
+// One page as loaded by the one-row kernel: line k of the page's 8 KB of
+// keys (1 KB, rows 8k .. 8k+7) spread over the wave, lane l holding bytes
+// [16l, 16l+16) of it, plus the scale of token `lane`. Each load instruction
+// reads whole 128-byte lines, which allows non-temporal loads: the keys are
+// read once, and streaming them past the caches reads faster than the
+// MFMA-layout loads below, whose instructions cover half lines.
+struct PageLines {
+  u32x4 v[8];
+  float ks;
+};
+
+__device__ __forceinline__ void load_page_lines(PageLines& pl, const uint8_t* base,
+                                                int lane) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    pl.v[k] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(base + k * 1024 + lane * 16));
+  pl.ks = __builtin_nontemporal_load(
+      reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane));
+}
+
+// Per-wave LDS image of one page of keys: 64 rows of 8 16-byte pieces, piece
+// p of row r stored at slot p ^ ((r >> 1) & 7), so that both the row-major
+// writes (2 rows per 16 lanes) and the MFMA-layout reads (16 rows, one piece)
+// of one ds_*_b128 cover all 64 banks once.
+__device__ __forceinline__ int key_lds(int r, int piece) {
+  return r * 8 + (piece ^ ((r >> 1) & 7));
+}
 
 // Keys of one page for this lane plus the scale of token `lane`. Always
 // issued (an absent page reads page 0 and its results are masked): a load
@@ -98,6 +138,7 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    int chunks_per_row, int pages_per_block, int group,
                    int64_t npairs, uint32_t* __restrict__ key_hist) {
   __shared__ uint32_t lhist[HIST ? kKeyBins : 1];
+  __shared__ u32x4 kst[kWaves][kPage * 8];   // per-wave page image, 8 KB each
   // block -> (row group, chunk) pair qi and row j of the group: the blocks
   // of one pair are `group` consecutive slots of one XCD's sequence (for
   // group 1 this is the plain order, qi = blockIdx.x)
@@ -155,19 +196,31 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
     const int id = __builtin_amdgcn_readlane(id_lane, i);
     return (id >= 0 && id < num_pages) ? id : -1;
   };
-  auto fetch = [&](PageKeys& pk, int i) {
+  auto fetch = [&](PageLines& pl, int i) {
     const int id = page_id(i);
-    load_page(pk, cache + (int64_t)(id >= 0 ? id : 0) * kPageBytesFp8, c, g, lane);
+    load_page_lines(pl, cache + (int64_t)(id >= 0 ? id : 0) * kPageBytesFp8, lane);
   };
-  auto score = [&](const PageKeys& pk, int i) {
+  u32x4* kl = kst[wave];
+  auto score = [&](const PageLines& pl, int i) {
+    // through the wave's LDS image into the MFMA layout: tile j, lane (c, g)
+    // takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row 16j + c. The
+    // wave's LDS instructions run in order, so the next page's writes cannot
+    // overtake these reads.
+#pragma unroll
+    for (int k = 0; k < 8; ++k) kl[key_lds(8 * k + (lane >> 3), lane & 7)] = pl.v[k];
+    wave_sync();
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const u32x4 lo = kl[key_lds(16 * j + c, g)];
+      const u32x4 hi = kl[key_lds(16 * j + c, 4 + g)];
+      const i32x8 kb = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       float s = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
         const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            qa[ht], pk.k[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            qa[ht], kb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) s = fmaf(wr[ht][r], relu(acc[r]), s);
       }
@@ -178,18 +231,19 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
     const float u0 = (b0 ? v[1] : v[0]) + __shfl_xor(b0 ? v[0] : v[1], 16);
     const float u1 = (b0 ? v[3] : v[2]) + __shfl_xor(b0 ? v[2] : v[3], 16);
     const float tot = (b1 ? u1 : u0) + __shfl_xor(b1 ? u0 : u1, 32);
-    const float result = page_id(i) >= 0 ? tot * pk.ks : -INFINITY;
+    const float result = page_id(i) >= 0 ? tot * pl.ks : -INFINITY;
     const int s = (first + kWaves * i) * kPage + lane;   // position of token `lane`
     if (i < np_w && s < L) {
       lrow[s] = result;
       if constexpr (HIST) atomicAdd(&lhist[order_key(result) >> 20], 1u);
     }
+    wave_sync();
   };
 
   // two page buffers: the keys of page i+1 are in flight while page i is
   // scored; a fetch past the wave's pages reads page 0 and is not stored
   if (np_w > 0) {
-    PageKeys b0, b1;
+    PageLines b0, b1;
     fetch(b0, 0);
     for (int i = 0; i < np_w; i += 2) {
       fetch(b1, i + 1);
