@@ -33,9 +33,10 @@
 //   * ReLU and the head weights are applied in registers; the 64-head sum is
 //     16 in-lane FMAs plus a 3-shuffle transpose-reduce that leaves token
 //     lane in lane `lane`, so each page is stored as 64 consecutive floats;
-//   * keys are loaded straight from HBM with 16-byte loads (each instruction
-//     reads 64 contiguous bytes of 16 key rows); the next page is in flight
-//     while one is scored, and no load sits under a branch.
+//   * keys are read as whole 128-byte lines (each 16-byte load instruction
+//     covers 1 KB of the page) with non-temporal loads, and each page passes
+//     through the wave's LDS image into the MFMA operand layout; the next
+//     page is in flight while one is scored, and no load sits under a branch.
 // The contraction dimension is split over lanes identically for q and for
 // the keys (each lane takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of a
 // 128-byte row, g = lane / 16), so the dot products do not depend on the
