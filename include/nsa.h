@@ -166,6 +166,10 @@ int nsa_build_metadata(int mode, int bs, int draft_token_num, int topk,
  *                    nsa_topk_transform; any stride is correct.
  * Supported: (fp8, Hi = 64, Di = 128) on the MFMA path; (fp32, Hi <= 64,
  * Di <= 128, Di % 4 == 0). page_size must be 64.
+ * The fp8 path assumes each key page is read by one row (decode) and streams
+ * the keys with non-temporal loads, which do not keep them in the caches;
+ * rows that share pages are served better by nsa_indexer_logits_hist with
+ * its rows_per_request hint. Results do not depend on this.
  */
 int nsa_indexer_logits(const void* q, int q_dtype, const float* weights,
                        const void* k_index_cache, int k_dtype,
@@ -222,7 +226,9 @@ int nsa_topk_transform(const float* logits, int64_t logits_stride,
  *   2 or 3   when T is a multiple of it, the blocks of a group that read
  *            the same key pages run back to back on one XCD, so the pages
  *            come from HBM about once per group;
- *   other    per-row order.
+ *   other    per-row order; at most 1 (one row per request, as in
+ *            decode) also streams the keys with non-temporal loads, which
+ *            do not keep them in the caches for other rows.
  * Every choice gives bit-identical logits and counts.
  *
  * nsa_topk_transform_hist: as nsa_topk_transform, with key_hist from

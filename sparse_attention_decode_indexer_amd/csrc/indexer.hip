@@ -34,7 +34,8 @@
 //     16 in-lane FMAs plus a 3-shuffle transpose-reduce that leaves token
 //     lane in lane `lane`, so each page is stored as 64 consecutive floats;
 //   * keys are read as whole 128-byte lines (each 16-byte load instruction
-//     covers 1 KB of the page) with non-temporal loads, and each page passes
+//     covers 1 KB of the page), non-temporal where each page has one reading
+//     row (rows_per_request <= 1), and each page passes
 //     through the wave's LDS image into the MFMA operand layout; the next
 //     page is in flight while one is scored, and no load sits under a branch.
 // The contraction dimension is split over lanes identically for q and for
@@ -74,22 +75,25 @@ struct PageKeys {
 // One page as loaded by the one-row kernel: line k of the page's 8 KB of
 // keys (1 KB, rows 8k .. 8k+7) spread over the wave, lane l holding bytes
 // [16l, 16l+16) of it, plus the scale of token `lane`. Each load instruction
-// reads whole 128-byte lines, which allows non-temporal loads: the keys are
-// read once, and streaming them past the caches reads faster than the
-// MFMA-layout loads below, whose instructions cover half lines.
+// reads whole 128-byte lines, which allows non-temporal loads (NT): where
+// each page has one reader, streaming the keys past the caches reads faster
+// than the MFMA-layout loads below, whose instructions cover half lines.
+// Where rows of one request share their pages, plain loads keep the pages
+// cached for the other rows.
 struct PageLines {
   u32x4 v[8];
   float ks;
 };
 
+template <bool NT>
 __device__ __forceinline__ void load_page_lines(PageLines& pl, const uint8_t* base,
                                                 int lane) {
+  const u32x4* kp = reinterpret_cast<const u32x4*>(base + lane * 16);
+  const float* sp = reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane);
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    pl.v[k] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(base + k * 1024 + lane * 16));
-  pl.ks = __builtin_nontemporal_load(
-      reinterpret_cast<const float*>(base + kPage * kDim + 4 * lane));
+    pl.v[k] = NT ? __builtin_nontemporal_load(kp + k * 64) : kp[k * 64];
+  pl.ks = NT ? __builtin_nontemporal_load(sp) : *sp;
 }
 
 // Per-wave LDS image of one page of keys: 64 rows of 8 16-byte pieces, piece
@@ -128,7 +132,7 @@ __device__ __forceinline__ float relu(float x) {
 // HIST: also count the top 12 bits of every written logit's order key into
 // key_hist[t][0..4095] (an LDS histogram per block, then one global atomic
 // per nonzero bin), so the top-k needs no pass of its own to histogram.
-template <bool HIST>
+template <bool HIST, bool NT>
 __global__ void __launch_bounds__(256)
 indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    const uint8_t* __restrict__ cache, int64_t num_pages,
@@ -199,7 +203,7 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
   };
   auto fetch = [&](PageLines& pl, int i) {
     const int id = page_id(i);
-    load_page_lines(pl, cache + (int64_t)(id >= 0 ? id : 0) * kPageBytesFp8, lane);
+    load_page_lines<NT>(pl, cache + (int64_t)(id >= 0 ? id : 0) * kPageBytesFp8, lane);
   };
   u32x4* kl = kst[wave];
   auto score = [&](const PageLines& pl, int i) {
@@ -563,7 +567,11 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
     const int64_t npairs = (int64_t)(T / group) * chunks_ppb;
     const int64_t blocks = (npairs + 7) / 8 * 8 * group;
     NSA_REQUIRE(blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
-    auto kern = key_hist ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>;
+    // non-temporal key loads only where no other row reads the same pages
+    // (nsa_indexer_logits, which has no hint, passes 1)
+    const bool nt = rows_per_request <= 1;
+    auto kern = !key_hist ? indexer_fp8_kernel<false, true>
+                          : (nt ? indexer_fp8_kernel<true, true> : indexer_fp8_kernel<true, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0,
                        s, static_cast<const uint8_t*>(q), weights,
                        static_cast<const uint8_t*>(k_index_cache), num_pages,
