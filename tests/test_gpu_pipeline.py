@@ -183,6 +183,14 @@ def test_indexer_row_groups_change_nothing(name, overrides):
         outs.append((lg.cpu(), kh.cpu()))
     for lg, kh in outs[1:]:
         assert torch.equal(lg, outs[0][0]) and torch.equal(kh, outs[0][1])
+    # the entry point without a histogram (and without a hint) writes the
+    # same logits
+    lg = torch.full((w.num_rows, nsa.logits_row_stride(w.max_seqlen_k)), 7.0, device=DEV)
+    nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
+                           md["real_page_table"], md["token_to_req"],
+                           md["seqlens_expanded"], w.max_seqlen_k, logits=lg)
+    torch.cuda.synchronize()
+    assert torch.equal(lg.cpu(), outs[0][0])
 
 
 def test_indexer_row_groups_with_unordered_rows():
