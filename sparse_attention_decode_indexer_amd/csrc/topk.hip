@@ -374,15 +374,19 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   // loads are issued now and land while the histogram is read and scanned
   const int vend = VEC ? (n & ~3) : n;
   constexpr int kSpan = kThreads * 4;           // positions per load step
-  constexpr int kPerBatch = kSpan * kBatch;
+  // the short-row instantiation takes half batches: with 64 registers a
+  // full batch pair spills, and each spill store waits for every load in
+  // flight (extend: 343 against 459 us)
+  constexpr int kB = SMALL ? kBatch / 2 : kBatch;
+  constexpr int kPerBatch = kSpan * kB;
   // last vector start; n >= 1 here, and a vector row (16-byte aligned,
   // stride a multiple of 4) always holds positions 0..3, so 0 is a safe
   // clamp for rows shorter than one vector
   const int vlast = vend >= 4 ? vend - 4 : 0;
-  float va[kBatch][4], vb[kBatch][4];
-  auto fetch = [&](float (&v)[kBatch][4], int b0) {
+  float va[kB][4], vb[kB][4];
+  auto fetch = [&](float (&v)[kB][4], int b0) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) load4<VEC>(row, b0 + j * kSpan + tid * 4, vlast, n, v[j]);
+    for (int j = 0; j < kB; ++j) load4<VEC>(row, b0 + j * kSpan + tid * 4, vlast, n, v[j]);
   };
   fetch(va, 0);   // no branch: a load under one would be waited for at once
 
@@ -429,7 +433,7 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
     return;
   }
 
-  // ---- one pass over the row, batches of kBatch loads per thread, the next
+  // ---- one pass over the row, batches of kB loads per thread, the next
   // batch in flight while one is classified (two register batches used in
   // turn). Loads past the row are clamped onto its last vector, so the
   // prefetch needs no branch.
@@ -460,10 +464,10 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
     // positions of keys in the bin are appended to the candidate store (a
     // loop over the set bits of a 16-bit mask; the keys are read back after
     // the pass).
-    auto classify = [&](const float (&v)[kBatch][4], int b0) {
+    auto classify = [&](const float (&v)[kB][4], int b0) {
       uint32_t cm = 0;   // bit 4j + e: candidate
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
+      for (int j = 0; j < kB; ++j) {
         const int pos = b0 + j * kSpan + tid * 4;
         uint32_t m = 0;
 #pragma unroll
