@@ -25,9 +25,47 @@ def test_topk_against_sort_and_partition(n, k):
         assert row[valid].min() >= kth
         part = np.argpartition(-row[:n], k - 1)[:k]
         assert set(part.tolist()) == set(valid.tolist())   # distinct scores
-        assert K.kth_largest(row, n, k) == kth
     else:
         np.testing.assert_array_equal(np.sort(valid), np.arange(n))
+
+
+def _kth_by_counting(row, n, k):
+    """The k-th largest of row[:n] from its definition alone: the value v of
+    the row such that fewer than k entries exceed v and at least k reach it
+    (O(n^2) comparisons, no sort)."""
+    x = np.asarray(row[:n], np.float64)
+    for v in x:
+        if (x > v).sum() < k <= (x >= v).sum():
+            return v
+    raise AssertionError("no k-th largest")
+
+
+@pytest.mark.parametrize("n,k", [(40, 1), (40, 7), (40, 39), (200, 64), (17, 16)])
+def test_kth_largest_against_definition_and_partition(n, k):
+    # kth_largest is the acceptance threshold of every top-k check; it is
+    # pinned by the counting definition, numpy's partition (a selection
+    # algorithm, not a sort) and the minimum of argpartition's k-set
+    rng = np.random.default_rng(100 * n + k)
+    row = np.concatenate([rng.normal(size=n), [1e30, -1e30]])   # tail ignored
+    got = K.kth_largest(row, n, k)
+    assert got == _kth_by_counting(row, n, k)
+    assert got == -np.partition(-row[:n], k - 1)[k - 1]
+    assert got == row[:n][np.argpartition(-row[:n], k - 1)[:k]].min()
+
+
+def test_kth_largest_hand_rows():
+    assert K.kth_largest([3.0, 1.0, 2.0], 3, 2) == 2.0
+    assert K.kth_largest([3.0, 1.0, 2.0], 3, 1) == 3.0
+    assert K.kth_largest([5.0, 5.0, 5.0, 1.0], 4, 2) == 5.0       # ties count
+    assert K.kth_largest([5.0, 5.0, 5.0, 1.0], 4, 3) == 5.0
+    assert K.kth_largest([-np.inf, 0.0, -1.0, 2.0], 4, 3) == -1.0
+    assert K.kth_largest([0.5, 9.0, 7.0, 8.0], 3, 2) == 7.0       # position 3 ignored
+    assert K.kth_largest([1.0, 2.0], 2, 2) == -np.inf              # keeps every position
+    assert K.kth_largest([1.0, 2.0], 2, 5) == -np.inf
+    # with ties, exactly the positions scoring >= the k-th value number >= k
+    row = np.array([4.0, 4.0, 3.0, 4.0, 1.0, 3.0])
+    v = K.kth_largest(row, 6, 4)
+    assert v == 3.0 and (row > v).sum() < 4 <= (row >= v).sum()
 
 
 def test_topk_ties_resolved_by_position():
