@@ -56,33 +56,61 @@ def parse():
 
 
 def indexer_cost(lengths, t2r, hi=64, di=128):
-    """Algorithmic bytes and flops of one indexer launch. Bytes: per row its
-    q row and weights and the fp32 logit of every position; per request the
-    fp8 key and fp32 scale of every position its longest row sees, and one
-    page-table entry per 64 of them (rows of one request read the same keys,
-    which need to come from HBM once). Flops: 2 * hi * di per (row,
-    position) for the dot products."""
+    """Strict algorithmic bytes, flops and logit bytes of one indexer launch.
+    Strict bytes: per row its q row and weights; per request the fp8 key and
+    fp32 scale of every position its longest row sees, and one page-table
+    entry per 64 of them (rows of one request read the same keys, which need
+    to come from HBM once). The fp32 logit written per (row, position) is an
+    intermediate (implementation traffic), returned apart. Flops: 2 * hi * di
+    per (row, position) for the dot products."""
     longest = {}
-    b = fl = 0
+    b = fl = lg = 0
     for L, r in zip(lengths, t2r):
         L = int(L)
-        b += hi * di + hi * 4 + L * 4
+        b += hi * di + hi * 4
+        lg += L * 4
         fl += 2 * hi * di * L
         longest[int(r)] = max(longest.get(int(r), 0), L)
     for L in longest.values():
         b += L * (di + 4) + ((L + 63) // 64) * 4
-    return b, fl
+    return b, fl, lg
 
 
 def pipeline_bytes(lengths, t2r, topk, heads, kv_row_bytes, hi=64, di=128):
     """Strict algorithmic bytes of one step: the indexer's (keys once per
     request), then per row the selected latent rows, MLA q and output."""
-    b, _ = indexer_cost(lengths, t2r, hi, di)
+    b, _, _ = indexer_cost(lengths, t2r, hi, di)
     for L in lengths:
         L = int(L)
-        b -= L * 4                               # logits are not strict bytes
         b += min(L, topk) * kv_row_bytes + heads * 576 * 2 + heads * 512 * 2 + heads * 4
     return b
+
+
+def measured_hbm(dev, gib=1, reps=5):
+    """HBM rates measured in this process on 1 GiB buffers (HIP events, best
+    of `reps`): a read-only pass (torch's sum over int32, reads 1 GiB) and a
+    copy (reads and writes 1 GiB each, counted as 2 GiB). GB/s."""
+    import torch
+    n = (gib << 30) // 4
+    a = torch.ones(n, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("read", lambda: a.sum(), n * 4),
+                             ("copy", lambda: b.copy_(a), 2 * n * 4)):
+        fn()
+        best = None
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        out[name] = nbytes / (best * 1e-3) / 1e9
+    del a, b
+    return out
 
 
 def read_pmc(expected_sha):
@@ -295,8 +323,9 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     se = md["seqlens_expanded"].cpu().numpy()     # visible length of every row
     t2r = md["token_to_req"].cpu().numpy()
-    idx_bytes, idx_flops = indexer_cost(se, t2r, w.idx_heads, w.idx_dim)
+    idx_bytes, idx_flops, idx_logit_bytes = indexer_cost(se, t2r, w.idx_heads, w.idx_dim)
     idx_ms = stage_ms[1]
+    meas = measured_hbm(dev)
     # the indexer's bound: HBM for its bytes or fp8 MFMA for its dot
     # products, whichever takes longer at peak
     if idx_flops / FP8_PEAK_TFLOPS > idx_bytes / HBM_PEAK_GBPS * 1e3:
@@ -306,6 +335,10 @@ def main():
         roof = {"bound": "hbm", "achieved": idx_bytes / (idx_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if roof["bound"] == "hbm":
+        # the same figure against this GPU's measured stream-read rate
+        roof["measured_peak"] = meas["read"]
+        roof["frac_of_measured"] = roof["achieved"] / meas["read"]
     pipe = pipeline_bytes(se, t2r, w.topk, w.heads, 656 if fp8_kv else 1152,
                           w.idx_heads, w.idx_dim)
     pipe_gbps = pipe / (ms_per_step * 1e-3) / 1e9
@@ -337,10 +370,17 @@ def main():
                    "indexer": f"{w.idx_heads}x{w.idx_dim} {w.idx_kind}",
                    "parallelism": "single GPU"},
         "roofline": dict(kernel=kernel, **roof, traffic=traffic,
+                         traffic_source=("rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel "
+                                         "source, committed in profiles/"
+                                         if traffic is not None else None),
                          algorithmic_bytes_per_launch=idx_bytes,
-                         algorithmic_flops_per_launch=idx_flops),
+                         algorithmic_flops_per_launch=idx_flops,
+                         implementation_bytes_per_launch=idx_logit_bytes),
         "pipeline": {"algorithmic_bytes_per_step": pipe, "GBps": pipe_gbps,
-                     "hbm_roofline_frac": pipe_gbps / HBM_PEAK_GBPS},
+                     "hbm_roofline_frac": pipe_gbps / HBM_PEAK_GBPS,
+                     "frac_of_measured_read": pipe_gbps / meas["read"]},
+        "measured_hbm_GBps": {"read": meas["read"], "copy": meas["copy"],
+                              "nominal": HBM_PEAK_GBPS},
         "stages_ms": {"metadata": stage_ms[0], "indexer": stage_ms[1],
                       "topk_transform": stage_ms[2], "sparse_mla": stage_ms[3]},
         "cpu_baseline": None,

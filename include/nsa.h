@@ -23,8 +23,10 @@
  *     checked on the host before anything is launched; on error nothing is
  *     launched and nsa_last_error() describes the problem. No call aborts.
  *   - Device-side data the host cannot check (index values, page ids, slot
- *     ids) is bounds-checked in the kernels: an out-of-range page id or slot
- *     is treated as absent (see each call), never dereferenced.
+ *     ids, request indices, pool rows) is bounds-checked in the kernels: an
+ *     out-of-range id is treated as absent (see each call), never
+ *     dereferenced, and recorded as an NSA_DEVERR_* bit that
+ *     nsa_check_device_errors() reports.
  */
 #ifndef NSA_H_
 #define NSA_H_
@@ -69,6 +71,32 @@ const char* nsa_last_error(void);
 /* Library version as an integer (major*10000 + minor*100 + patch). */
 int nsa_version(void);
 
+/* ---- device-side errors ------------------------------------------------------
+ * The DSA page validates the page table against the KV-cache capacity before
+ * an extend ([dsa-main] init_forward_metadata, extend branch: the largest
+ * token slot must lie below the pool's capacity). Here every kernel checks
+ * the ids it reads from device memory and, for one out of range, records
+ * one of these bits in a device word (one per library translation unit, per
+ * device) while treating the id as absent:
+ */
+#define NSA_DEVERR_PAGE_ID 0x1   /* indexer: a page id outside [0, num_pages) */
+#define NSA_DEVERR_SLOT 0x2      /* a KV slot outside [0, num_slots) other than -1
+                                    (attention, quantize-on-write, paged
+                                    dequantisation) */
+#define NSA_DEVERR_REQUEST 0x4   /* a token_to_req entry outside [0, rows of the
+                                    page table) (indexer, top-k, transform,
+                                    ragged metadata) */
+#define NSA_DEVERR_POOL_ROW 0x8  /* metadata: a req_pool_indices entry outside
+                                    [0, pool_rows) */
+#define NSA_DEVERR_INDEX 0x10    /* transform: a top-k index at or past its
+                                    table's width */
+/* Waits for `stream`, then returns the OR of the NSA_DEVERR_* bits recorded
+ * on the current device since the last call (>= 0) and clears them, or a
+ * negative status if the HIP runtime fails. It synchronises with the host, so
+ * it belongs in debug paths and tests, not inside a captured graph. Calls
+ * that overlap on other streams may add bits while it runs. */
+int nsa_check_device_errors(void* stream);
+
 /* ---- a0: per-forward metadata ------------------------------------------------
  * Defined by [nsa-fork] NSAMetadata, compute_cu_seqlens,
  * _transform_table_1_to_real and NativeSparseAttnBackend.init_forward_metadata;
@@ -86,7 +114,9 @@ int nsa_version(void);
  *   extend_lens[bs]       new tokens per request (EXTEND and DRAFT_EXTEND,
  *                         else ignored / NULL).
  *   req_to_token          [pool_rows, rtt_stride] token -> physical slot.
- *   req_pool_indices[bs]  each request's row of req_to_token.
+ *   req_pool_indices[bs]  each request's row of req_to_token; a row outside
+ *                         [0, pool_rows) gives -1 page ids in its tables
+ *                         (NSA_DEVERR_POOL_ROW).
  * Host scalars:
  *   mode                  NSA_MODE_*.
  *   draft_token_num       tokens per request of TARGET_VERIFY and
@@ -96,7 +126,11 @@ int nsa_version(void);
  *   max_seqlen_k          host bound >= every cache seqlen; sizes the tables.
  *   num_q_rows            T: bs (decode), bs*draft (verify, draft-extend
  *                         v2), sum of extend_lens (extend, draft-extend).
- *                         Rows past T are never written.
+ *                         Extend modes: rows past sum(extend_lens) get
+ *                         length 0 (seqlens_expanded, nsa_cache_seqlens),
+ *                         token_to_req 0 and the running
+ *                         nsa_cu_seqlens_k total, so a T above the sum is
+ *                         harmless; rows past T are never written.
  * Outputs (device, int32, caller-allocated):
  *   cache_seqlens[bs]         seq_lens (+ draft_token_num in verify).
  *   cu_seqlens_k[bs+1]        [0, cumsum(cache_seqlens)].
@@ -126,7 +160,8 @@ int nsa_version(void);
 int nsa_build_metadata(int mode, int bs, int draft_token_num, int topk,
                        int page_size, const int32_t* seq_lens,
                        const int32_t* extend_lens, const int32_t* req_to_token,
-                       int64_t rtt_stride, const int32_t* req_pool_indices,
+                       int64_t rtt_stride, int64_t pool_rows,
+                       const int32_t* req_pool_indices,
                        int max_seqlen_k, int num_q_rows,
                        int32_t* cache_seqlens, int32_t* cu_seqlens_k,
                        int32_t* cu_seqlens_q, int32_t* seqlens_expanded,
@@ -155,11 +190,14 @@ int nsa_build_metadata(int mode, int bs, int draft_token_num, int topk,
  *   k_index_cache    [num_pages] pages of 64 tokens; page bytes =
  *                    64*Di*elem (keys, row-major [64][Di]) + 64*4 (fp32
  *                    per-token scales). k_dtype must equal q_dtype.
- *   real_page_table  [*, rpt_stride] page ids per request; a page id outside
- *                    [0, num_pages) yields -inf logits for its 64 positions.
+ *   real_page_table  [num_reqs, rpt_stride] page ids per request; a page id
+ *                    outside [0, num_pages) yields -inf logits for its 64
+ *                    positions (NSA_DEVERR_PAGE_ID).
  *                    The fp8 path needs num_pages >= 1 (it reads page 0 in
  *                    place of an absent page); 0 is NSA_ERR_INVALID_ARG there.
- *   token_to_req[T], seqlens_expanded[T]  from nsa_build_metadata.
+ *   token_to_req[T], seqlens_expanded[T]  from nsa_build_metadata; a row
+ *                    whose token_to_req lies outside [0, num_reqs) is left
+ *                    unwritten, as an empty row (NSA_DEVERR_REQUEST).
  *   logits           [T, logits_stride] fp32, logits_stride >= max_seqlen_k.
  *                    Rows that start 256-byte aligned (stride a multiple of
  *                    64) give whole-line stores here and vector loads in
@@ -174,7 +212,7 @@ int nsa_build_metadata(int mode, int bs, int draft_token_num, int topk,
 int nsa_indexer_logits(const void* q, int q_dtype, const float* weights,
                        const void* k_index_cache, int k_dtype,
                        int64_t num_pages, const int32_t* real_page_table,
-                       int64_t rpt_stride, const int32_t* token_to_req,
+                       int64_t rpt_stride, int64_t num_reqs, const int32_t* token_to_req,
                        const int32_t* seqlens_expanded, int T, int Hi, int Di,
                        int page_size, int max_seqlen_k, float* logits,
                        int64_t logits_stride, void* stream);
@@ -191,8 +229,10 @@ int nsa_indexer_logits(const void* q, int q_dtype, const float* weights,
  * the threshold are broken by ascending position. NaN logits rank lowest.
  *   table == NULL    out holds logical positions.
  *   table != NULL    out holds physical slots: table is the compact page
- *                    table [*, table_stride] (real_page_table) and
- *                    slot = table[token_to_req[t], i >> 6] * 64 + (i & 63).
+ *                    table [table_rows, table_stride] (real_page_table) and
+ *                    slot = table[token_to_req[t], i >> 6] * 64 + (i & 63);
+ *                    a row whose token_to_req lies outside [0, table_rows)
+ *                    is written as all -1 (NSA_DEVERR_REQUEST).
  *   workspace        device scratch of nsa_topk_workspace_size() bytes (may
  *                    be NULL when that size is 0).
  */
@@ -200,7 +240,7 @@ int nsa_topk_workspace_size(int T, int max_seqlen_k, int topk, size_t* bytes);
 int nsa_topk_transform(const float* logits, int64_t logits_stride,
                        const int32_t* lengths, int T, int topk,
                        int max_seqlen_k, const int32_t* table,
-                       int64_t table_stride, const int32_t* token_to_req,
+                       int64_t table_stride, int64_t table_rows, const int32_t* token_to_req,
                        int page_size, int32_t* out, int64_t out_stride,
                        void* workspace, size_t ws_bytes, void* stream);
 
@@ -242,7 +282,7 @@ int nsa_topk_transform(const float* logits, int64_t logits_stride,
 int nsa_indexer_logits_hist(const void* q, int q_dtype, const float* weights,
                             const void* k_index_cache, int k_dtype,
                             int64_t num_pages, const int32_t* real_page_table,
-                            int64_t rpt_stride, const int32_t* token_to_req,
+                            int64_t rpt_stride, int64_t num_reqs, const int32_t* token_to_req,
                             const int32_t* seqlens_expanded, int T, int Hi,
                             int Di, int page_size, int max_seqlen_k,
                             float* logits, int64_t logits_stride,
@@ -251,7 +291,7 @@ int nsa_indexer_logits_hist(const void* q, int q_dtype, const float* weights,
 int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
                             const int32_t* lengths, int T, int topk,
                             int max_seqlen_k, const int32_t* table,
-                            int64_t table_stride, const int32_t* token_to_req,
+                            int64_t table_stride, int64_t table_rows, const int32_t* token_to_req,
                             int page_size, uint32_t* key_hist, int32_t* out,
                             int64_t out_stride, void* stream);
 
@@ -261,15 +301,18 @@ int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
  * page_size=1). out[t, j] = -1 if idx < 0, else the physical slot of logical
  * position idx of request token_to_req[t]: page_table_1[r, idx] (wide form)
  * or real_page_table[r, idx >> 6] * 64 + (idx & 63) (compact form). Exactly
- * one of page_table_1 / real_page_table must be non-NULL. Indices at or past
- * the table width give -1.
+ * one of page_table_1 / real_page_table must be non-NULL, with table_rows
+ * rows. Indices at or past the table width give -1 (NSA_DEVERR_INDEX); a row
+ * whose token_to_req lies outside [0, table_rows) is written as all -1
+ * (NSA_DEVERR_REQUEST).
  */
 int nsa_page_table_transform(const int32_t* topk_indices, int64_t in_stride,
                              int T, int topk, const int32_t* page_table_1,
                              int64_t pt1_stride, int64_t pt1_width,
                              const int32_t* real_page_table,
                              int64_t rpt_stride, int64_t rpt_width,
-                             int page_size, const int32_t* token_to_req,
+                             int64_t table_rows, int page_size,
+                             const int32_t* token_to_req,
                              int32_t* out, int64_t out_stride, void* stream);
 
 /* ---- a4 / a5: sparse MLA over selected slots ------------------------------------
@@ -284,7 +327,8 @@ int nsa_page_table_transform(const int32_t* topk_indices, int64_t in_stride,
  *   kv_cache     [num_slots] rows: NSA_KV_BF16_576 (576 bf16) or
  *                NSA_KV_FP8_656 (the quantize_k_cache layout).
  *   indices      [T, idx_stride] int32 physical slots, -1 = unused; a slot
- *                outside [0, num_slots) counts as unused.
+ *                outside [0, num_slots) counts as unused (and, unless -1,
+ *                sets NSA_DEVERR_SLOT).
  *   nsa_cache_seqlens  optional [T]: only the first nsa_cache_seqlens[t]
  *                entries of row t are read (NULL: all topk entries).
  *   out          [T, H, 512] bf16, contiguous.
@@ -344,8 +388,8 @@ int nsa_quantize_k_cache(const void* kv_bf16, int64_t num_slots,
  *   k_rope      [n, rope_stride] bf16, first 64 elements used; bf16 cache:
  *               16-byte aligned, rope_stride a multiple of 8.
  *   cache_loc   [n] int32 destination slots; entries outside
- *               [0, num_slots) are skipped. Entries must be distinct (two
- *               rows to one slot race).
+ *               [0, num_slots) are skipped (NSA_DEVERR_SLOT). Entries must
+ *               be distinct (two rows to one slot race).
  *   kv_cache    [num_slots, 656] bytes or [num_slots, 576] bf16, updated in
  *               place; other slots are not touched.
  * Nothing is allocated; n == 0 is a no-op.
@@ -402,7 +446,7 @@ int nsa_ragged_index_transform(const int32_t* topk_indices, int64_t in_stride,
  * NSA_KV_FP8_656 cache: each no-rope value = fp32 product of its e4m3 code
  * and block scale, rounded to bf16 (nearest even); the 64 rope values copied;
  * a slot outside [0, num_slots) gives a zero row (a reading: the body is not
- * on the pages). out: [n, out_stride] bf16, out_stride >= 576 and a multiple
+ * on the pages; NSA_DEVERR_SLOT). out: [n, out_stride] bf16, out_stride >= 576 and a multiple
  * of 8, 16-byte aligned. */
 int nsa_dequantize_k_cache_paged(const void* kv_fp8, int64_t num_slots,
                                  const int32_t* slots, int64_t n, void* out,

@@ -109,9 +109,16 @@ def nsa_build_metadata(mode, seq_lens, req_to_token, req_pool_indices, topk,
             if out[k].shape[0] < bs or out[k].shape[1] < cols:
                 raise ValueError(f"out[{k!r}] must be at least [{bs}, {cols}]")
     pt1 = out.get("page_table_1") if want_page_table_1 else None
+    if req_pool_indices.numel() < bs:
+        raise ValueError("req_pool_indices needs an entry per request")
+    if extend_lens is not None and extend_lens.numel() < bs:
+        raise ValueError("extend_lens needs an entry per request")
+    if bs and req_to_token.shape[1] < max_seqlen_k:
+        raise ValueError("req_to_token needs max_seqlen_k columns")
     call("nsa_build_metadata", mode, bs, draft_token_num, topk, page_size,
          _ptr(seq_lens), _ptr(extend_lens), _ptr(req_to_token),
-         req_to_token.stride(0), _ptr(req_pool_indices), max_seqlen_k, T,
+         req_to_token.stride(0), req_to_token.shape[0], _ptr(req_pool_indices),
+         max_seqlen_k, T,
          _ptr(out["cache_seqlens"]), _ptr(out["cu_seqlens_k"]),
          _ptr(out["cu_seqlens_q"]), _ptr(out["seqlens_expanded"]),
          _ptr(out["nsa_cache_seqlens"]), _ptr(out["nsa_cu_seqlens_k"]),
@@ -154,14 +161,22 @@ def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
     _check(token_to_req, "token_to_req", torch.int32, 1)
     _check(seqlens_expanded, "seqlens_expanded", torch.int32, 1)
     T, Hi, Di = q.shape
+    if tuple(weights.shape) != (T, Hi):
+        raise ValueError(f"weights must be [{T}, {Hi}]")
+    if token_to_req.numel() < T or seqlens_expanded.numel() < T:
+        raise ValueError("token_to_req / seqlens_expanded need an entry per row")
+    if real_page_table.shape[1] < (max_seqlen_k + PAGE_SIZE - 1) // PAGE_SIZE:
+        raise ValueError("real_page_table needs ceil(max_seqlen_k / 64) columns")
     if logits is None:
         logits = torch.empty(T, logits_row_stride(max_seqlen_k),
                              dtype=torch.float32, device=q.device)
     _check(logits, "logits", torch.float32, 2, contiguous=False)
+    if logits.shape[0] < T or logits.shape[1] < max_seqlen_k or logits.stride(1) != 1:
+        raise ValueError(f"logits must be [>= {T}, >= {max_seqlen_k}] with unit column stride")
     args = (_ptr(q), dtype, _ptr(weights), _ptr(index_cache), dtype,
             index_cache.shape[0], _ptr(real_page_table), real_page_table.stride(0),
-            _ptr(token_to_req), _ptr(seqlens_expanded), T, Hi, Di, PAGE_SIZE,
-            max_seqlen_k, _ptr(logits), logits.stride(0))
+            real_page_table.shape[0], _ptr(token_to_req), _ptr(seqlens_expanded),
+            T, Hi, Di, PAGE_SIZE, max_seqlen_k, _ptr(logits), logits.stride(0))
     if key_hist is None:
         call("nsa_indexer_logits", *args, _stream())
     else:
@@ -183,12 +198,21 @@ def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
     T = lengths.numel()
     if logits is not None:
         _check(logits, "logits", torch.float32, 2, contiguous=False)
+        if logits.shape[0] < T or logits.shape[1] < max_seqlen_k or logits.stride(1) != 1:
+            raise ValueError(f"logits must be [>= {T}, >= {max_seqlen_k}] with unit column stride")
     if table is not None:
         _check(table, "table", torch.int32, 2)
         _check(token_to_req, "token_to_req", torch.int32, 1)
+        if token_to_req.numel() < T:
+            raise ValueError("token_to_req needs an entry per row")
+        if table.shape[1] < (max_seqlen_k + PAGE_SIZE - 1) // PAGE_SIZE:
+            raise ValueError("table needs ceil(max_seqlen_k / 64) columns")
     if out is None:
         out = torch.empty(T, topk, dtype=torch.int32, device=lengths.device)
     _check(out, "out", torch.int32, 2, contiguous=False)
+    if out.shape[0] < T or out.shape[1] < topk or out.stride(1) != 1:
+        raise ValueError(f"out must be [>= {T}, >= {topk}] with unit column stride")
+    trows = table.shape[0] if table is not None else 0
     if key_hist is not None:
         _check(key_hist, "key_hist", torch.int32, 2)
         if key_hist.shape[0] < T or key_hist.shape[1] != KEY_BINS:
@@ -196,8 +220,8 @@ def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
         call("nsa_topk_transform_hist", _ptr(logits),
              logits.stride(0) if logits is not None else 0, _ptr(lengths), T, topk,
              max_seqlen_k, _ptr(table), table.stride(0) if table is not None else 0,
-             _ptr(token_to_req), PAGE_SIZE, _ptr(key_hist), _ptr(out), out.stride(0),
-             _stream())
+             trows, _ptr(token_to_req), PAGE_SIZE, _ptr(key_hist), _ptr(out),
+             out.stride(0), _stream())
         return out
     ws = ctypes.c_size_t(0)
     call("nsa_topk_workspace_size", T, max_seqlen_k, topk, ctypes.byref(ws))
@@ -206,7 +230,7 @@ def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
     call("nsa_topk_transform", _ptr(logits),
          logits.stride(0) if logits is not None else 0, _ptr(lengths), T, topk,
          max_seqlen_k, _ptr(table), table.stride(0) if table is not None else 0,
-         _ptr(token_to_req), PAGE_SIZE, _ptr(out), out.stride(0), _ptr(work),
+         trows, _ptr(token_to_req), PAGE_SIZE, _ptr(out), out.stride(0), _ptr(work),
          ws.value, _stream())
     return out
 
@@ -217,18 +241,30 @@ def nsa_page_table_transform(topk_indices, token_to_req, page_table_1=None,
     _check(topk_indices, "topk_indices", torch.int32, 2, contiguous=False)
     _check(token_to_req, "token_to_req", torch.int32, 1)
     T, K = topk_indices.shape
+    if token_to_req.numel() < T:
+        raise ValueError("token_to_req needs an entry per row")
+    if topk_indices.stride(1) != 1:
+        raise ValueError("topk_indices must have unit column stride")
     if out is None:
         out = torch.empty(T, K, dtype=torch.int32, device=topk_indices.device)
-    pt1_stride = pt1_width = rpt_stride = rpt_width = 0
+    _check(out, "out", torch.int32, 2, contiguous=False)
+    if out.shape[0] < T or out.shape[1] < K or out.stride(1) != 1:
+        raise ValueError(f"out must be [>= {T}, >= {K}] with unit column stride")
+    pt1_stride = pt1_width = rpt_stride = rpt_width = rows = 0
+    for tab in (page_table_1, real_page_table):
+        if tab is not None and tab.stride(1) != 1:
+            raise ValueError("page tables must have unit column stride")
     if page_table_1 is not None:
         _check(page_table_1, "page_table_1", torch.int32, 2, contiguous=False)
         pt1_stride, pt1_width = page_table_1.stride(0), page_table_1.shape[1]
+        rows = page_table_1.shape[0]
     if real_page_table is not None:
         _check(real_page_table, "real_page_table", torch.int32, 2, contiguous=False)
         rpt_stride, rpt_width = real_page_table.stride(0), real_page_table.shape[1]
+        rows = real_page_table.shape[0]
     call("nsa_page_table_transform", _ptr(topk_indices), topk_indices.stride(0),
          T, K, _ptr(page_table_1), pt1_stride, pt1_width, _ptr(real_page_table),
-         rpt_stride, rpt_width, PAGE_SIZE, _ptr(token_to_req), _ptr(out),
+         rpt_stride, rpt_width, rows, PAGE_SIZE, _ptr(token_to_req), _ptr(out),
          out.stride(0), _stream())
     return out
 
@@ -253,10 +289,21 @@ def _sparse_mla(name, q, kv_cache, kv_dtype, indices, sm_scale,
     if nsa_cache_seqlens is not None:
         _check(nsa_cache_seqlens, "nsa_cache_seqlens", torch.int32, 1)
     topk = indices.shape[1]
+    if indices.shape[0] < T or indices.stride(1) != 1:
+        raise ValueError(f"indices must be [>= {T}, topk] with unit column stride")
+    if nsa_cache_seqlens is not None and nsa_cache_seqlens.numel() < T:
+        raise ValueError("nsa_cache_seqlens needs an entry per row")
     if out is None:
         out = torch.empty(T, H, D_V, dtype=torch.bfloat16, device=q.device)
+    _check(out, "out", torch.bfloat16, 3)
+    if tuple(out.shape) != (T, H, D_V):
+        raise ValueError(f"out must be [{T}, {H}, {D_V}]")
     if lse is None and want_lse:
         lse = torch.empty(T, H, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (T, H):
+            raise ValueError(f"lse must be [{T}, {H}]")
     need = sparse_mla_workspace_size(T, H, topk)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -283,6 +330,22 @@ def nsa_sparse_mla_extend(q, kv_cache, kv_dtype, indices, sm_scale,
     """Sparse MLA for many query rows (chunked extend)."""
     return _sparse_mla("nsa_sparse_mla_extend", q, kv_cache, kv_dtype, indices,
                        sm_scale, nsa_cache_seqlens, out, lse, workspace, want_lse)
+
+
+def nsa_check_device_errors():
+    """Waits for the current stream and returns (then clears) the
+    NSA_DEVERR_* bits the kernels recorded on this device: 0 when no kernel
+    met an out-of-range id. Synchronises with the host: for tests and debug
+    paths, not for captured graphs."""
+    lib = load()
+    st = lib.nsa_check_device_errors(_stream())
+    if st < 0:
+        raise NsaError("nsa_check_device_errors", st, lib.nsa_last_error().decode())
+    return st
+
+
+DEVERR_PAGE_ID, DEVERR_SLOT, DEVERR_REQUEST, DEVERR_POOL_ROW, DEVERR_INDEX = (
+    0x1, 0x2, 0x4, 0x8, 0x10)
 
 
 def nsa_quantize_k_cache(kv_bf16, out=None):

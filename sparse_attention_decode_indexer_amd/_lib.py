@@ -4,7 +4,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libnsa.so")
+# NSA_LIB_PATH selects another build of the same library (the host-sanitizer
+# build of the CPU tests); the default is the in-tree libnsa.so
+LIB_PATH = os.environ.get("NSA_LIB_PATH") or os.path.join(_PKG, "libnsa.so")
 
 c_int, c_i64, c_f32, c_size = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 P = ctypes.c_void_p
@@ -13,23 +15,24 @@ P = ctypes.c_void_p
 SIGNATURES = {
     "nsa_last_error": (ctypes.c_char_p, []),
     "nsa_version": (c_int, []),
+    "nsa_check_device_errors": (c_int, [P]),
     "nsa_build_metadata": (c_int, [
-        c_int, c_int, c_int, c_int, c_int, P, P, P, c_i64, P, c_int, c_int,
+        c_int, c_int, c_int, c_int, c_int, P, P, P, c_i64, c_i64, P, c_int, c_int,
         P, P, P, P, P, P, P, P, c_i64, P, P, c_i64, P]),
     "nsa_indexer_logits": (c_int, [
-        P, c_int, P, P, c_int, c_i64, P, c_i64, P, P, c_int, c_int, c_int,
+        P, c_int, P, P, c_int, c_i64, P, c_i64, c_i64, P, P, c_int, c_int, c_int,
         c_int, c_int, P, c_i64, P]),
     "nsa_indexer_logits_hist": (c_int, [
-        P, c_int, P, P, c_int, c_i64, P, c_i64, P, P, c_int, c_int, c_int,
+        P, c_int, P, P, c_int, c_i64, P, c_i64, c_i64, P, P, c_int, c_int, c_int,
         c_int, c_int, P, c_i64, P, c_int, P]),
     "nsa_topk_workspace_size": (c_int, [c_int, c_int, c_int, ctypes.POINTER(c_size)]),
     "nsa_topk_transform_hist": (c_int, [
-        P, c_i64, P, c_int, c_int, c_int, P, c_i64, P, c_int, P, P, c_i64, P]),
+        P, c_i64, P, c_int, c_int, c_int, P, c_i64, c_i64, P, c_int, P, P, c_i64, P]),
     "nsa_topk_transform": (c_int, [
-        P, c_i64, P, c_int, c_int, c_int, P, c_i64, P, c_int, P, c_i64, P,
+        P, c_i64, P, c_int, c_int, c_int, P, c_i64, c_i64, P, c_int, P, c_i64, P,
         c_size, P]),
     "nsa_page_table_transform": (c_int, [
-        P, c_i64, c_int, c_int, P, c_i64, c_i64, P, c_i64, c_i64, c_int, P, P,
+        P, c_i64, c_int, c_int, P, c_i64, c_i64, P, c_i64, c_i64, c_i64, c_int, P, P,
         c_i64, P]),
     "nsa_sparse_mla_workspace_size": (c_int, [c_int, c_int, c_int, c_int,
                                               ctypes.POINTER(c_size)]),

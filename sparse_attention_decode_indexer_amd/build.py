@@ -58,9 +58,21 @@ def _finish(proc, what, verbose):
         print(out)
 
 
-def build_library(verbose=False, extra_flags=()):
-    """Compiles every source to an object (in parallel), then links them."""
-    objdir = os.path.join(PKG_DIR, "_build")
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer: every option is
+# scoped to the host compilation with -Xarch_host, so the gfx950 code objects
+# are built as usual (GPU sanitizers are not used). For the CPU tests of the
+# C ABI's argument checks (tests/test_host_sanitizers.py).
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address,undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def build_library(verbose=False, extra_flags=(), lib_path=None, objdir=None,
+                  link_flags=()):
+    """Compiles every source to an object (in parallel), then links them.
+    lib_path / objdir default to the in-tree libnsa.so and _build/."""
+    lib_path = lib_path or LIB_PATH
+    objdir = objdir or os.path.join(PKG_DIR, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs, procs = [], []
     for src in SOURCES:
@@ -71,11 +83,17 @@ def build_library(verbose=False, extra_flags=()):
         procs.append((_run(cmd, verbose), src))
     for proc, src in procs:
         _finish(proc, src, verbose)
-    tmp = LIB_PATH + ".tmp"
-    _finish(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
-                 verbose), "link", verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    tmp = lib_path + ".tmp"
+    _finish(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_flags, *objs,
+                  "-o", tmp], verbose), "link", verbose)
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build_host_sanitized(lib_path, objdir, verbose=False):
+    """The same library with host ASan + UBSan (see HOST_SANITIZE)."""
+    return build_library(verbose, extra_flags=HOST_SANITIZE, lib_path=lib_path,
+                         objdir=objdir, link_flags=HOST_SANITIZE)
 
 
 if __name__ == "__main__":

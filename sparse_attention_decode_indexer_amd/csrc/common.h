@@ -33,6 +33,43 @@ inline bool aligned(const void* p, size_t a) {
 
 }  // namespace nsa
 
+// ---- device-side error word -----------------------------------------------
+// Ids the host cannot see (page ids, slots, request indices, pool rows) are
+// checked in the kernels; an out-of-range one is treated as absent and its
+// NSA_DEVERR_* bit is OR-ed into a word in device memory with a vector
+// atomic. The library is built without relocatable device code, so every
+// translation unit has its own word; each unit registers a reader at load
+// time and nsa_check_device_errors() combines (and clears) them all.
+static __device__ uint32_t nsa_device_error_word;
+
+__device__ __forceinline__ void flag_device_error(uint32_t bits) {
+  atomicOr(&nsa_device_error_word, bits);
+}
+
+namespace nsa {
+typedef int (*ErrorReader)(hipStream_t, uint32_t*);
+// Adds a reader to the library's list; returns its index.
+int register_error_reader(ErrorReader f);
+}  // namespace nsa
+
+// Reads and clears this unit's word on the current device (synchronises s).
+static int nsa_take_unit_errors(hipStream_t s, uint32_t* bits) {
+  uint32_t v = 0;
+  const uint32_t zero = 0;
+  if (hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(nsa_device_error_word), sizeof(v), 0,
+                               hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return -1;
+  if (v != 0 && (hipMemcpyToSymbolAsync(HIP_SYMBOL(nsa_device_error_word), &zero,
+                                        sizeof(zero), 0, hipMemcpyHostToDevice, s) != hipSuccess ||
+                 hipStreamSynchronize(s) != hipSuccess))
+    return -1;
+  *bits = v;
+  return 0;
+}
+__attribute__((used)) static const int nsa_unit_reader_index =
+    nsa::register_error_reader(nsa_take_unit_errors);
+
 #define NSA_REQUIRE(cond, code, ...)              \
   do {                                            \
     if (!(cond)) return nsa::set_error(code, __VA_ARGS__); \

@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(256)
 indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                    const uint8_t* __restrict__ cache, int64_t num_pages,
                    const int32_t* __restrict__ rpt, int64_t rpt_stride,
-                   const int32_t* __restrict__ t2r,
+                   int64_t num_reqs, const int32_t* __restrict__ t2r,
                    const int32_t* __restrict__ seqlens, int max_seqlen_k,
                    float* __restrict__ logits, int64_t logits_stride,
                    int chunks_per_row, int pages_per_block, int group,
@@ -158,6 +158,12 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
   const int p_begin = chunk * pages_per_block;
   if (p_begin >= npages) return;
   const int p_end = min(p_begin + pages_per_block, npages);
+  // a row of no known request stays unwritten (an empty row)
+  const int32_t req = t2r[t];
+  if (req < 0 || req >= num_reqs) {
+    if (chunk == 0 && threadIdx.x == 0) flag_device_error(NSA_DEVERR_REQUEST);
+    return;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -182,7 +188,7 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
     wr[ht][0] = v.x; wr[ht][1] = v.y; wr[ht][2] = v.z; wr[ht][3] = v.w;
   }
 
-  const int32_t* prow = rpt + (int64_t)t2r[t] * rpt_stride;
+  const int32_t* prow = rpt + (int64_t)req * rpt_stride;
   float* lrow = logits + t * logits_stride;
 
   if constexpr (HIST) {
@@ -196,6 +202,7 @@ indexer_fp8_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
   const int first = p_begin + wave;
   const int np_w = first < p_end ? (p_end - first + kWaves - 1) / kWaves : 0;
   const int id_lane = lane < np_w ? prow[first + kWaves * lane] : -1;
+  if (lane < np_w && (id_lane < 0 || id_lane >= num_pages)) flag_device_error(NSA_DEVERR_PAGE_ID);
 
   auto page_id = [&](int i) -> int {   // -1: absent or invalid
     const int id = __builtin_amdgcn_readlane(id_lane, i);
@@ -301,7 +308,7 @@ __global__ void __launch_bounds__(256)
 indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__ w,
                         const uint8_t* __restrict__ cache, int64_t num_pages,
                         const int32_t* __restrict__ rpt, int64_t rpt_stride,
-                        const int32_t* __restrict__ t2r,
+                        int64_t num_reqs, const int32_t* __restrict__ t2r,
                         const int32_t* __restrict__ seqlens, int max_seqlen_k,
                         int64_t T, float* __restrict__ logits,
                         int64_t logits_stride, int chunks_per_group,
@@ -322,8 +329,13 @@ indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__
   for (int r = 0; r < kRows; ++r) {
     int L = r < nrows ? seqlens[t0 + r] : 0;
     L = L < 0 ? 0 : (L > max_seqlen_k ? max_seqlen_k : L);
+    int rq = r < nrows ? t2r[t0 + r] : -1;
+    if (L > 0 && (rq < 0 || rq >= num_reqs)) {   // no known request: an empty row
+      if (chunk == 0 && threadIdx.x == 0) flag_device_error(NSA_DEVERR_REQUEST);
+      L = 0;
+    }
     Lr[r] = L;
-    req[r] = r < nrows ? t2r[t0 + r] : -1;
+    req[r] = L > 0 ? rq : -1;
     uniform = uniform && (r >= nrows || req[r] == req[0]);
     Lmax = max(Lmax, L);
   }
@@ -362,6 +374,7 @@ indexer_fp8_rows_kernel(const uint8_t* __restrict__ q, const float* __restrict__
     const int first = p_begin + wave;
     const int np_w = first < p_end ? (p_end - first + kWaves - 1) / kWaves : 0;
     const int id_lane = lane < np_w ? prow[first + kWaves * lane] : -1;
+    if (lane < np_w && (id_lane < 0 || id_lane >= num_pages)) flag_device_error(NSA_DEVERR_PAGE_ID);
 
     auto page_id = [&](int i) -> int {   // -1: absent or invalid
       const int id = __builtin_amdgcn_readlane(id_lane, i);
@@ -461,7 +474,7 @@ __global__ void __launch_bounds__(256)
 indexer_fp32_kernel(const float* __restrict__ q, const float* __restrict__ w,
                     const uint8_t* __restrict__ cache, int64_t num_pages,
                     const int32_t* __restrict__ rpt, int64_t rpt_stride,
-                    const int32_t* __restrict__ t2r,
+                    int64_t num_reqs, const int32_t* __restrict__ t2r,
                     const int32_t* __restrict__ seqlens, int max_seqlen_k,
                     float* __restrict__ logits, int64_t logits_stride, int Hi,
                     int Di, int chunks_per_row) {
@@ -478,9 +491,16 @@ indexer_fp32_kernel(const float* __restrict__ q, const float* __restrict__ w,
   for (int i = threadIdx.x; i < Hi; i += 256) ws[i] = w[t * Hi + i];
   __syncthreads();
   if (s >= L) return;
-  const int page = rpt[(int64_t)t2r[t] * rpt_stride + s / kPage];
+  const int32_t req = t2r[t];
+  if (req < 0 || req >= num_reqs) {   // no known request: an empty row
+    if (chunk == 0 && threadIdx.x == 0) flag_device_error(NSA_DEVERR_REQUEST);
+    return;
+  }
+  const int page = rpt[(int64_t)req * rpt_stride + s / kPage];
   float out = -INFINITY;
-  if (page >= 0 && page < num_pages) {
+  if (page < 0 || page >= num_pages) {
+    if (s % kPage == 0) flag_device_error(NSA_DEVERR_PAGE_ID);
+  } else {
     const int64_t page_bytes = (int64_t)kPage * Di * 4 + kPage * 4;
     const uint8_t* base = cache + page * page_bytes;
     const float* k = reinterpret_cast<const float*>(base) + (s % kPage) * Di;
@@ -503,11 +523,12 @@ namespace {
 int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights,
                 const void* k_index_cache, int k_dtype, int64_t num_pages,
                 const int32_t* real_page_table, int64_t rpt_stride,
-                const int32_t* token_to_req, const int32_t* seqlens_expanded,
+                int64_t num_reqs, const int32_t* token_to_req,
+                const int32_t* seqlens_expanded,
                 int T, int Hi, int Di, int page_size, int max_seqlen_k,
                 float* logits, int64_t logits_stride, uint32_t* key_hist,
                 int rows_per_request, void* stream) {
-  NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0 && num_pages >= 0,
+  NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0 && num_pages >= 0 && num_reqs >= 0,
               NSA_ERR_INVALID_ARG, "%s: negative size", fn);
   NSA_REQUIRE(page_size == NSA_PAGE_SIZE, NSA_ERR_UNSUPPORTED,
               "%s: page_size %d (only 64 is supported)", fn, page_size);
@@ -552,7 +573,7 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
       hipLaunchKernelGGL(indexer_fp8_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                          static_cast<const uint8_t*>(q), weights,
                          static_cast<const uint8_t*>(k_index_cache), num_pages,
-                         real_page_table, rpt_stride, token_to_req,
+                         real_page_table, rpt_stride, num_reqs, token_to_req,
                          seqlens_expanded, max_seqlen_k, (int64_t)T, logits,
                          logits_stride, rchunks, key_hist);
       return nsa::check_launch(fn);
@@ -575,7 +596,7 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0,
                        s, static_cast<const uint8_t*>(q), weights,
                        static_cast<const uint8_t*>(k_index_cache), num_pages,
-                       real_page_table, rpt_stride, token_to_req,
+                       real_page_table, rpt_stride, num_reqs, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits, logits_stride,
                        chunks_ppb, ppb, group, npairs, key_hist);
   } else {
@@ -586,7 +607,7 @@ int indexer_run(const char* fn, const void* q, int q_dtype, const float* weights
     hipLaunchKernelGGL(indexer_fp32_kernel, dim3((unsigned)blocks), dim3(256),
                        shm, s, static_cast<const float*>(q), weights,
                        static_cast<const uint8_t*>(k_index_cache), num_pages,
-                       real_page_table, rpt_stride, token_to_req,
+                       real_page_table, rpt_stride, num_reqs, token_to_req,
                        seqlens_expanded, max_seqlen_k, logits, logits_stride,
                        Hi, Di, chunks);
   }
@@ -600,14 +621,14 @@ extern "C" int nsa_indexer_logits(const void* q, int q_dtype,
                                   const void* k_index_cache, int k_dtype,
                                   int64_t num_pages,
                                   const int32_t* real_page_table,
-                                  int64_t rpt_stride,
+                                  int64_t rpt_stride, int64_t num_reqs,
                                   const int32_t* token_to_req,
                                   const int32_t* seqlens_expanded, int T,
                                   int Hi, int Di, int page_size,
                                   int max_seqlen_k, float* logits,
                                   int64_t logits_stride, void* stream) {
   return indexer_run("nsa_indexer_logits", q, q_dtype, weights, k_index_cache,
-                     k_dtype, num_pages, real_page_table, rpt_stride,
+                     k_dtype, num_pages, real_page_table, rpt_stride, num_reqs,
                      token_to_req, seqlens_expanded, T, Hi, Di, page_size,
                      max_seqlen_k, logits, logits_stride, nullptr, 1, stream);
 }
@@ -617,7 +638,7 @@ extern "C" int nsa_indexer_logits_hist(const void* q, int q_dtype,
                                        const void* k_index_cache, int k_dtype,
                                        int64_t num_pages,
                                        const int32_t* real_page_table,
-                                       int64_t rpt_stride,
+                                       int64_t rpt_stride, int64_t num_reqs,
                                        const int32_t* token_to_req,
                                        const int32_t* seqlens_expanded, int T,
                                        int Hi, int Di, int page_size,
@@ -628,7 +649,8 @@ extern "C" int nsa_indexer_logits_hist(const void* q, int q_dtype,
   NSA_REQUIRE(T == 0 || key_hist != nullptr, NSA_ERR_INVALID_ARG,
               "%s: null key_hist", fn);
   return indexer_run(fn, q, q_dtype, weights, k_index_cache, k_dtype, num_pages,
-                     real_page_table, rpt_stride, token_to_req, seqlens_expanded,
+                     real_page_table, rpt_stride, num_reqs, token_to_req,
+                     seqlens_expanded,
                      T, Hi, Di, page_size, max_seqlen_k, logits, logits_stride,
                      key_hist, rows_per_request, stream);
 }

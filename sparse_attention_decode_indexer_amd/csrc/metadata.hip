@@ -65,7 +65,7 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
                       const int32_t* __restrict__ seq_lens,
                       const int32_t* __restrict__ extend_lens,
                       const int32_t* __restrict__ req_to_token,
-                      int64_t rtt_stride,
+                      int64_t rtt_stride, int64_t pool_rows,
                       const int32_t* __restrict__ req_pool_indices,
                       int max_seqlen_k, int T, int32_t* cache_seqlens,
                       int32_t* cu_seqlens_k, int32_t* cu_seqlens_q,
@@ -85,14 +85,19 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
     const int chunks = (ncols + kThreads - 1) / kThreads;
     const int b = blockIdx.x - nreq_blocks;
     const int r = b / chunks, c = b % chunks;
-    const int32_t* row = req_to_token + (int64_t)req_pool_indices[r] * rtt_stride;
+    // a pool row outside req_to_token gives -1 (absent) entries
+    const int32_t pr = req_pool_indices[r];
+    const bool pr_ok = pr >= 0 && pr < pool_rows;
+    if (!pr_ok && c == 0 && tid == 0) flag_device_error(NSA_DEVERR_POOL_ROW);
+    const int32_t* row = req_to_token + (int64_t)(pr_ok ? pr : 0) * rtt_stride;
     const int p = c * kThreads + tid;
-    if (p < ncols) real_page_table[(int64_t)r * rpt_stride + p] = row[(int64_t)p * NSA_PAGE_SIZE] >> 6;
+    if (p < ncols)
+      real_page_table[(int64_t)r * rpt_stride + p] = pr_ok ? row[(int64_t)p * NSA_PAGE_SIZE] >> 6 : -1;
     if (page_table_1 != nullptr) {
       int32_t* pt = page_table_1 + (int64_t)r * pt1_stride;
       const int c0 = c * kThreads * NSA_PAGE_SIZE;
       const int c1 = min(c0 + kThreads * NSA_PAGE_SIZE, max_seqlen_k);
-      for (int k = c0 + tid; k < c1; k += kThreads) pt[k] = row[k];
+      for (int k = c0 + tid; k < c1; k += kThreads) pt[k] = pr_ok ? row[k] : -1;
     }
     return;
   }
@@ -138,7 +143,20 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
     token_to_req[t] = r;
     if (mode != NSA_MODE_EXTEND) cu_seqlens_q[t + 1] = (int32_t)(t + 1);
   }
-
+  // extend modes: the rows from the end of the last request up to T (a host
+  // bound above sum(extend_lens)) become empty rows of request 0
+  if (r == bs - 1) {
+    const long long t_end = pq + ql;
+    const long long n_end = pn + clipped_sum(a, ql, topk);
+    for (long long t = t_end + tid; t < T; t += kThreads) {
+      seqlens_expanded[t] = 0;
+      nsa_cache_seqlens[t] = 0;
+      nsa_cu_seqlens_k[t + 1] = (int32_t)n_end;
+      nsa_cu_seqlens_q[t + 1] = (int32_t)(t + 1);
+      token_to_req[t] = 0;
+      if (mode != NSA_MODE_EXTEND) cu_seqlens_q[t + 1] = (int32_t)(t + 1);
+    }
+  }
 }
 
 }  // namespace
@@ -146,7 +164,7 @@ build_metadata_kernel(int mode, int bs, int draft, int topk,
 extern "C" int nsa_build_metadata(
     int mode, int bs, int draft_token_num, int topk, int page_size,
     const int32_t* seq_lens, const int32_t* extend_lens,
-    const int32_t* req_to_token, int64_t rtt_stride,
+    const int32_t* req_to_token, int64_t rtt_stride, int64_t pool_rows,
     const int32_t* req_pool_indices, int max_seqlen_k, int num_q_rows,
     int32_t* cache_seqlens, int32_t* cu_seqlens_k, int32_t* cu_seqlens_q,
     int32_t* seqlens_expanded, int32_t* nsa_cache_seqlens,
@@ -175,6 +193,8 @@ extern "C" int nsa_build_metadata(
   } else {
     NSA_REQUIRE(extend_lens != nullptr, NSA_ERR_INVALID_ARG,
                 "%s: extend and draft-extend need extend_lens", fn);
+    NSA_REQUIRE(bs > 0 || num_q_rows == 0, NSA_ERR_INVALID_ARG,
+                "%s: an empty batch has no query rows", fn);
   }
   // buffers of zero length may be NULL (an empty batch has no rows)
   NSA_REQUIRE(cu_seqlens_k && cu_seqlens_q && nsa_cu_seqlens_k && nsa_cu_seqlens_q,
@@ -194,6 +214,8 @@ extern "C" int nsa_build_metadata(
               (long long)rpt_stride, (long long)ncols);
   NSA_REQUIRE(page_table_1 == nullptr || pt1_stride >= max_seqlen_k,
               NSA_ERR_INVALID_ARG, "%s: pt1_stride < max_seqlen_k", fn);
+  NSA_REQUIRE(bs == 0 || pool_rows >= 1, NSA_ERR_INVALID_ARG,
+              "%s: pool_rows %lld < 1", fn, (long long)pool_rows);
 
   const int64_t chunks = (ncols + kThreads - 1) / kThreads;
   const int64_t grid = (bs > 0 ? bs : 1) + (int64_t)bs * chunks;
@@ -201,7 +223,7 @@ extern "C" int nsa_build_metadata(
   hipLaunchKernelGGL(build_metadata_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, mode, bs, draft_token_num, topk,
                      seq_lens, extend_lens, req_to_token, rtt_stride,
-                     req_pool_indices, max_seqlen_k, num_q_rows, cache_seqlens,
+                     pool_rows, req_pool_indices, max_seqlen_k, num_q_rows, cache_seqlens,
                      cu_seqlens_k, cu_seqlens_q, seqlens_expanded,
                      nsa_cache_seqlens, nsa_cu_seqlens_k, nsa_cu_seqlens_q,
                      real_page_table, rpt_stride, token_to_req, page_table_1,

@@ -69,7 +69,9 @@ __device__ __forceinline__ int64_t dest_slot(const int32_t* cache_loc, int64_t i
                                              int64_t num_slots) {
   if constexpr (SCATTER) {
     const int64_t s = cache_loc[i];
-    return (s >= 0 && s < num_slots) ? s : -1;
+    if (s >= 0 && s < num_slots) return s;
+    flag_device_error(NSA_DEVERR_SLOT);
+    return -1;
   } else {
     return i;
   }
@@ -146,6 +148,7 @@ dequantize_paged_kernel(const uint8_t* __restrict__ cache, int64_t num_slots,
   if (i >= n) return;
   const int64_t slot = slots[i];
   const bool ok = slot >= 0 && slot < num_slots;
+  if (!ok && lane == 0) flag_device_error(NSA_DEVERR_SLOT);
   const uint8_t* row = cache + (ok ? slot : 0) * 656;
   uint16_t* orow = out + i * out_stride;
   uint4 v = make_uint4(0, 0, 0, 0);

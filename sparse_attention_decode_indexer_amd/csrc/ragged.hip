@@ -29,7 +29,9 @@ ragged_rows_kernel(const int32_t* __restrict__ cu_seqlens_k, int bs,
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (t >= T) return;
   const int r = token_to_req[t];
-  const int32_t s = (r >= 0 && r < bs) ? cu_seqlens_k[r] : 0;
+  const bool r_ok = r >= 0 && r < bs;
+  if (!r_ok) flag_device_error(NSA_DEVERR_REQUEST);
+  const int32_t s = r_ok ? cu_seqlens_k[r] : 0;
   ks[t] = s;
   ke[t] = s + seqlens_expanded[t];
   if (offset) offset[t] = s;

@@ -243,6 +243,7 @@ sparse_mla_kernel(const Params p) {
     return in ? id : -1;
   };
   auto publish_ids = [&](int buf, int32_t id) {
+    if (id < -1 || id >= p.num_slots) flag_device_error(NSA_DEVERR_SLOT);
     if (id < 0 || id >= p.num_slots) id = -1;
     if (tid < kStep) ids[buf][tid] = id;
     if (wave == 0) {
@@ -633,6 +634,7 @@ sparse_mla_h64_kernel(const Params p) {
     for (int k = 0; k < kIdsCap / kThreadsW; ++k) {
       const int i = tid + k * kThreadsW;
       const int32_t id = v[k];
+      if (i < n && (id < -1 || id >= p.num_slots)) flag_device_error(NSA_DEVERR_SLOT);
       ids[i] = (i < n && id >= 0 && id < p.num_slots) ? id : -1;
     }
   }

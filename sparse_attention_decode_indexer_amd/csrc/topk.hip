@@ -338,8 +338,8 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
                    const uint16_t* __restrict__ ws,
                    uint32_t* __restrict__ key_hist,
                    const int32_t* __restrict__ table, int64_t table_stride,
-                   const int32_t* __restrict__ t2r, int32_t* __restrict__ out,
-                   int64_t out_stride) {
+                   int64_t table_rows, const int32_t* __restrict__ t2r,
+                   int32_t* __restrict__ out, int64_t out_stride) {
   constexpr int kMB = SMALL ? kSmallMapBits : kMapBits;   // bitmap bits
   constexpr int kMW = kMB / 32;
   constexpr int kCP = SMALL ? 4096 : kCap;                 // candidate store
@@ -357,12 +357,20 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
   int n = lengths[t];
   n = n < 0 ? 0 : (n > max_seqlen_k ? max_seqlen_k : n);
   int32_t* orow = out + t * out_stride;
-  const int32_t* trow = table ? table + (int64_t)t2r[t] * table_stride : nullptr;
+  static_assert(kThreads * 4 == kHistBins && kHistBins == kKeyBins, "one thread per 4 bins");
+  uint4* hrow4 = GIVEN ? reinterpret_cast<uint4*>(key_hist + t * kHistBins) : nullptr;
+  const int32_t req = table ? t2r[t] : 0;
+  if (table && (req < 0 || req >= table_rows)) {
+    // a row of no known request has no slots: all -1
+    if (tid == 0) flag_device_error(NSA_DEVERR_REQUEST);
+    for (int j = tid; j < topk; j += kThreads) orow[j] = -1;
+    if (GIVEN) hrow4[tid] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  const int32_t* trow = table ? table + (int64_t)req * table_stride : nullptr;
   auto map = [&](int i) -> int32_t {
     return trow ? (trow[i >> 6] << 6) + (i & 63) : i;
   };
-  static_assert(kThreads * 4 == kHistBins && kHistBins == kKeyBins, "one thread per 4 bins");
-  uint4* hrow4 = GIVEN ? reinterpret_cast<uint4*>(key_hist + t * kHistBins) : nullptr;
   if (n <= topk) {
     for (int j = tid; j < topk; j += kThreads) orow[j] = j < n ? map(j) : -1;
     if (GIVEN) hrow4[tid] = make_uint4(0, 0, 0, 0);
@@ -629,7 +637,7 @@ extern "C" int nsa_topk_workspace_size(int T, int max_seqlen_k, int topk,
 extern "C" int nsa_topk_transform(const float* logits, int64_t logits_stride,
                                   const int32_t* lengths, int T, int topk,
                                   int max_seqlen_k, const int32_t* table,
-                                  int64_t table_stride,
+                                  int64_t table_stride, int64_t table_rows,
                                   const int32_t* token_to_req, int page_size,
                                   int32_t* out, int64_t out_stride,
                                   void* workspace, size_t ws_bytes,
@@ -653,6 +661,7 @@ extern "C" int nsa_topk_transform(const float* logits, int64_t logits_stride,
                 "%s: a table needs token_to_req", fn);
     NSA_REQUIRE(table_stride >= (max_seqlen_k + 63) / 64, NSA_ERR_INVALID_ARG,
                 "%s: table_stride < ceil(max_seqlen_k/64)", fn);
+    NSA_REQUIRE(table_rows >= 0, NSA_ERR_INVALID_ARG, "%s: negative table_rows", fn);
   }
   size_t need = 0;
   nsa_topk_workspace_size(T, max_seqlen_k, topk, &need);
@@ -680,14 +689,14 @@ extern "C" int nsa_topk_transform(const float* logits, int64_t logits_stride,
                  : (small ? topk_select_kernel<false, false, true> : topk_select_kernel<false, false, false>);
   hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, s, logits, logits_stride,
                      lengths, topk, max_seqlen_k, chunks, ws, nullptr, table,
-                     table_stride, token_to_req, out, out_stride);
+                     table_stride, table_rows, token_to_req, out, out_stride);
   return nsa::check_launch(fn);
 }
 
 extern "C" int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
                                        const int32_t* lengths, int T, int topk,
                                        int max_seqlen_k, const int32_t* table,
-                                       int64_t table_stride,
+                                       int64_t table_stride, int64_t table_rows,
                                        const int32_t* token_to_req, int page_size,
                                        uint32_t* key_hist, int32_t* out,
                                        int64_t out_stride, void* stream) {
@@ -712,6 +721,7 @@ extern "C" int nsa_topk_transform_hist(const float* logits, int64_t logits_strid
                 "%s: a table needs token_to_req", fn);
     NSA_REQUIRE(table_stride >= (max_seqlen_k + 63) / 64, NSA_ERR_INVALID_ARG,
                 "%s: table_stride < ceil(max_seqlen_k/64)", fn);
+    NSA_REQUIRE(table_rows >= 0, NSA_ERR_INVALID_ARG, "%s: negative table_rows", fn);
   }
   const bool vec = logits && nsa::aligned(logits, 16) && logits_stride % 4 == 0;
   const bool small = max_seqlen_k <= kSmallMapBits && T >= kSmallMinRows;
@@ -719,7 +729,7 @@ extern "C" int nsa_topk_transform_hist(const float* logits, int64_t logits_strid
                  : (small ? topk_select_kernel<false, true, true> : topk_select_kernel<false, true, false>);
   hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, (hipStream_t)stream,
                      logits, logits_stride, lengths, topk, max_seqlen_k, 0,
-                     nullptr, key_hist, table, table_stride, token_to_req, out,
-                     out_stride);
+                     nullptr, key_hist, table, table_stride, table_rows,
+                     token_to_req, out, out_stride);
   return nsa::check_launch(fn);
 }

@@ -22,9 +22,14 @@ __device__ __forceinline__ int32_t map_one(int32_t i, const int32_t* pt1_row,
                                            const int32_t* rpt_row,
                                            int64_t rpt_width) {
   if (i < 0) return -1;
-  if (pt1_row != nullptr) return i < pt1_width ? pt1_row[i] : -1;
-  const int32_t p = i >> 6;
-  return p < rpt_width ? (rpt_row[p] << 6) + (i & 63) : -1;
+  if (pt1_row != nullptr) {
+    if (i < pt1_width) return pt1_row[i];
+  } else {
+    const int32_t p = i >> 6;
+    if (p < rpt_width) return (rpt_row[p] << 6) + (i & 63);
+  }
+  flag_device_error(NSA_DEVERR_INDEX);   // past the table's width
+  return -1;
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -33,16 +38,23 @@ page_table_transform_kernel(const int32_t* __restrict__ idx, int64_t in_stride,
                             const int32_t* __restrict__ pt1, int64_t pt1_stride,
                             int64_t pt1_width, const int32_t* __restrict__ rpt,
                             int64_t rpt_stride, int64_t rpt_width,
+                            int64_t table_rows,
                             const int32_t* __restrict__ t2r, int32_t* out,
                             int64_t out_stride, bool vec) {
   const int64_t t = blockIdx.x / chunks_per_row;
   const int c = blockIdx.x % chunks_per_row;
   const int32_t r = t2r[t];
-  const int32_t* pt1_row = pt1 ? pt1 + (int64_t)r * pt1_stride : nullptr;
-  const int32_t* rpt_row = rpt ? rpt + (int64_t)r * rpt_stride : nullptr;
   const int32_t* in = idx + t * in_stride;
   int32_t* o = out + t * out_stride;
   const int j0 = c * kChunk + threadIdx.x * kPerThread;
+  if (r < 0 || r >= table_rows) {   // a row of no known request: all -1
+    if (c == 0 && threadIdx.x == 0) flag_device_error(NSA_DEVERR_REQUEST);
+    for (int k = 0; k < kPerThread; ++k)
+      if (j0 + k < topk) o[j0 + k] = -1;
+    return;
+  }
+  const int32_t* pt1_row = pt1 ? pt1 + (int64_t)r * pt1_stride : nullptr;
+  const int32_t* rpt_row = rpt ? rpt + (int64_t)r * rpt_stride : nullptr;
   if (vec && j0 + kPerThread <= topk) {
     const int4 v = *reinterpret_cast<const int4*>(in + j0);
     int4 w;
@@ -65,10 +77,11 @@ extern "C" int nsa_page_table_transform(
     const int32_t* topk_indices, int64_t in_stride, int T, int topk,
     const int32_t* page_table_1, int64_t pt1_stride, int64_t pt1_width,
     const int32_t* real_page_table, int64_t rpt_stride, int64_t rpt_width,
-    int page_size, const int32_t* token_to_req, int32_t* out,
-    int64_t out_stride, void* stream) {
+    int64_t table_rows, int page_size, const int32_t* token_to_req,
+    int32_t* out, int64_t out_stride, void* stream) {
   const char* fn = "nsa_page_table_transform";
-  NSA_REQUIRE(T >= 0 && topk >= 0, NSA_ERR_INVALID_ARG, "%s: negative size", fn);
+  NSA_REQUIRE(T >= 0 && topk >= 0 && table_rows >= 0, NSA_ERR_INVALID_ARG,
+              "%s: negative size", fn);
   NSA_REQUIRE(page_size == NSA_PAGE_SIZE, NSA_ERR_UNSUPPORTED,
               "%s: page_size %d (only 64 is supported)", fn, page_size);
   NSA_REQUIRE((page_table_1 == nullptr) != (real_page_table == nullptr),
@@ -94,6 +107,6 @@ extern "C" int nsa_page_table_transform(
                      dim3(kThreads), 0, (hipStream_t)stream, topk_indices,
                      in_stride, topk, chunks, page_table_1, pt1_stride,
                      pt1_width, real_page_table, rpt_stride, rpt_width,
-                     token_to_req, out, out_stride, vec);
+                     table_rows, token_to_req, out, out_stride, vec);
   return nsa::check_launch(fn);
 }

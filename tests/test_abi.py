@@ -49,23 +49,23 @@ def _err(lib):
 def test_metadata_rejects_bad_arguments(lib):
     out = [ctypes.c_void_p(16)] * 8
     # unknown mode
-    assert lib.nsa_build_metadata(7, 1, 0, 8, 64, 16, N, 16, 64, 16, 64, 1,
+    assert lib.nsa_build_metadata(7, 1, 0, 8, 64, 16, N, 16, 64, 4, 16, 64, 1,
                                   *out, 1, 16, N, 0, N) == -1
     assert "mode" in _err(lib)
     # page size
-    assert lib.nsa_build_metadata(0, 1, 0, 8, 32, 16, N, 16, 64, 16, 64, 1,
+    assert lib.nsa_build_metadata(0, 1, 0, 8, 32, 16, N, 16, 64, 4, 16, 64, 1,
                                   *out, 1, 16, N, 0, N) == -2
     # decode needs num_q_rows == bs
-    assert lib.nsa_build_metadata(0, 2, 0, 8, 64, 16, N, 16, 64, 16, 64, 3,
+    assert lib.nsa_build_metadata(0, 2, 0, 8, 64, 16, N, 16, 64, 4, 16, 64, 3,
                                   *out, 1, 16, N, 0, N) == -1
     # verify needs bs * draft rows
-    assert lib.nsa_build_metadata(2, 2, 3, 8, 64, 16, N, 16, 64, 16, 64, 5,
+    assert lib.nsa_build_metadata(2, 2, 3, 8, 64, 16, N, 16, 64, 4, 16, 64, 5,
                                   *out, 1, 16, N, 0, N) == -1
     # extend needs extend_lens
-    assert lib.nsa_build_metadata(1, 2, 0, 8, 64, 16, N, 16, 64, 16, 64, 5,
+    assert lib.nsa_build_metadata(1, 2, 0, 8, 64, 16, N, 16, 64, 4, 16, 64, 5,
                                   *out, 1, 16, N, 0, N) == -1
     # real_page_table stride too small for max_seqlen_k = 200 (needs 4)
-    assert lib.nsa_build_metadata(0, 1, 0, 8, 64, 16, N, 16, 256, 16, 200, 1,
+    assert lib.nsa_build_metadata(0, 1, 0, 8, 64, 16, N, 16, 256, 4, 16, 200, 1,
                                   *out, 3, 16, N, 0, N) == -1
     assert "rpt_stride" in _err(lib)
 
@@ -73,41 +73,41 @@ def test_metadata_rejects_bad_arguments(lib):
 def test_indexer_rejects_bad_arguments(lib):
     p = ctypes.c_void_p(256)
     # fp8 path supports only 64 heads x 128 dims
-    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 10, p, 4, p, p, 4, 32, 128, 64,
+    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 10, p, 4, 4, p, p, 4, 32, 128, 64,
                                   200, p, 256, N) == -2
     # mismatched dtypes
-    assert lib.nsa_indexer_logits(p, 2, p, p, 0, 10, p, 4, p, p, 4, 64, 128, 64,
+    assert lib.nsa_indexer_logits(p, 2, p, p, 0, 10, p, 4, 4, p, p, 4, 64, 128, 64,
                                   200, p, 256, N) == -2
     # logits stride below max_seqlen_k
-    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 10, p, 4, p, p, 4, 64, 128, 64,
+    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 10, p, 4, 4, p, p, 4, 64, 128, 64,
                                   200, p, 100, N) == -1
     # misaligned q
-    assert lib.nsa_indexer_logits(ctypes.c_void_p(257), 2, p, p, 2, 10, p, 4, p,
+    assert lib.nsa_indexer_logits(ctypes.c_void_p(257), 2, p, p, 2, 10, p, 4, 4, p,
                                   p, 4, 64, 128, 64, 200, p, 256, N) == -1
     # the fp8 path reads page 0 in place of an absent page: an empty cache
     # is rejected (also with the row-group hint)
-    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 0, p, 4, p, p, 4, 64, 128, 64,
+    assert lib.nsa_indexer_logits(p, 2, p, p, 2, 0, p, 4, 4, p, p, 4, 64, 128, 64,
                                   200, p, 256, N) == -1
     assert "num_pages" in _err(lib)
-    assert lib.nsa_indexer_logits_hist(p, 2, p, p, 2, 0, p, 4, p, p, 4, 64, 128, 64,
+    assert lib.nsa_indexer_logits_hist(p, 2, p, p, 2, 0, p, 4, 4, p, p, 4, 64, 128, 64,
                                        200, p, 256, p, 4, N) == -1
 
 
 def test_topk_and_transform_reject_bad_arguments(lib):
     p = ctypes.c_void_p(256)
-    assert lib.nsa_topk_transform(p, 100, p, 4, 0, 100, N, 0, N, 64, p, 16, N, 0,
+    assert lib.nsa_topk_transform(p, 100, p, 4, 0, 100, N, 0, 4, N, 64, p, 16, N, 0,
                                   N) == -1                      # topk 0
-    assert lib.nsa_topk_transform(p, 100, p, 4, 16, 100, p, 1, p, 64, p, 16, N, 0,
+    assert lib.nsa_topk_transform(p, 100, p, 4, 16, 100, p, 1, 4, p, 64, p, 16, N, 0,
                                   N) == -1                      # table stride
-    assert lib.nsa_topk_transform(p, 100, p, 4, 16, 100, N, 0, N, 64, p, 8, N, 0,
+    assert lib.nsa_topk_transform(p, 100, p, 4, 16, 100, N, 0, 4, N, 64, p, 8, N, 0,
                                   N) == -1                      # out stride
     # exactly one table
-    assert lib.nsa_page_table_transform(p, 8, 2, 8, p, 8, 8, p, 8, 8, 64, p, p, 8,
+    assert lib.nsa_page_table_transform(p, 8, 2, 8, p, 8, 8, p, 8, 8, 4, 64, p, p, 8,
                                         N) == -1
-    assert lib.nsa_page_table_transform(p, 8, 2, 8, N, 0, 0, N, 0, 0, 64, p, p, 8,
+    assert lib.nsa_page_table_transform(p, 8, 2, 8, N, 0, 0, N, 0, 0, 4, 64, p, p, 8,
                                         N) == -1
     # zero rows is a no-op
-    assert lib.nsa_topk_transform(N, 0, N, 0, 8, 0, N, 0, N, 64, N, 8, N, 0, N) == 0
+    assert lib.nsa_topk_transform(N, 0, N, 0, 8, 0, N, 0, 4, N, 64, N, 8, N, 0, N) == 0
     ws = ctypes.c_size_t(99)
     assert lib.nsa_topk_workspace_size(4, 100, 16, ctypes.byref(ws)) == 0
 
@@ -174,14 +174,14 @@ def test_binding_refuses_cpu_tensors():
 def test_fused_histogram_entry_points_validate(lib):
     P = ctypes.c_void_p
     # null key_hist
-    assert lib.nsa_indexer_logits_hist(P(16), 2, P(16), P(16), 2, 10, P(16), 4, P(16),
+    assert lib.nsa_indexer_logits_hist(P(16), 2, P(16), P(16), 2, 10, P(16), 4, 4, P(16),
                                        P(16), 1, 64, 128, 64, 256, P(16), 256, N, 1, N) == -1
     assert "key_hist" in _err(lib)
     # the histogram needs the fp8 path
-    assert lib.nsa_indexer_logits_hist(P(16), 0, P(16), P(16), 0, 10, P(16), 4, P(16),
+    assert lib.nsa_indexer_logits_hist(P(16), 0, P(16), P(16), 0, 10, P(16), 4, 4, P(16),
                                        P(16), 1, 4, 64, 64, 256, P(16), 256, P(16), 1, N) == -2
     # misaligned key_hist for the top-k
-    assert lib.nsa_topk_transform_hist(P(16), 256, P(16), 1, 64, 256, N, 0, N, 64,
+    assert lib.nsa_topk_transform_hist(P(16), 256, P(16), 1, 64, 256, N, 0, 4, N, 64,
                                        P(18), P(16), 64, N) == -1
     assert "aligned" in _err(lib)
 
@@ -217,13 +217,13 @@ def test_empty_batches_launch_nothing(lib):
     # before it touches a pointer, so NULL buffers are accepted
     P = ctypes.c_void_p
     f = ctypes.c_float
-    assert lib.nsa_indexer_logits(N, 2, N, N, 2, 10, N, 4, N, N, 0, 64, 128, 64,
+    assert lib.nsa_indexer_logits(N, 2, N, N, 2, 10, N, 4, 4, N, N, 0, 64, 128, 64,
                                   256, N, 256, N) == 0
-    assert lib.nsa_indexer_logits_hist(N, 2, N, N, 2, 10, N, 4, N, N, 0, 64, 128, 64,
+    assert lib.nsa_indexer_logits_hist(N, 2, N, N, 2, 10, N, 4, 4, N, N, 0, 64, 128, 64,
                                        256, N, 256, N, 1, N) == 0
-    assert lib.nsa_topk_transform(N, 0, N, 0, 64, 256, N, 0, N, 64, N, 64, N, 0, N) == 0
-    assert lib.nsa_topk_transform_hist(N, 0, N, 0, 64, 256, N, 0, N, 64, N, N, 64, N) == 0
-    assert lib.nsa_page_table_transform(N, 64, 0, 64, N, 0, 0, P(16), 4, 4, 64, N, N,
+    assert lib.nsa_topk_transform(N, 0, N, 0, 64, 256, N, 0, 4, N, 64, N, 64, N, 0, N) == 0
+    assert lib.nsa_topk_transform_hist(N, 0, N, 0, 64, 256, N, 0, 4, N, 64, N, N, 64, N) == 0
+    assert lib.nsa_page_table_transform(N, 64, 0, 64, N, 0, 0, P(16), 4, 4, 4, 64, N, N,
                                         64, N) == 0
     for entry in (lib.nsa_sparse_mla_decode, lib.nsa_sparse_mla_extend):
         assert entry(N, 0, 576, N, 0, 0, N, 64, N, 0, 16, 64, 576, 512, f(0.1),

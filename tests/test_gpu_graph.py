@@ -5,18 +5,21 @@ bit for bit, also after the request lengths are refreshed in place between
 replays (no host sync, no re-capture) -- the graph-capturable metadata of
 "nsa_backend.py (EngineX-Hygon sglang fork)", init_forward_metadata_replay_
 cuda_graph, and "dsa_backend.py (sglang main)", the static metadata buffers
-updated in place. Eager work and synchronisations run between the replays."""
+updated in place. Eager work and synchronisations run between the replays.
+Every replay, the refreshed ones included, is also checked against the
+oracle on rows spread over the requests: metadata bit-exact, logits, the
+top-k acceptance, slots and attention."""
 
 import pytest
 import torch
 
 import workloads as W
-from helpers import DEV, need_gpu, note, idx_dtype
+from helpers import DEV, need_gpu, note, idx_dtype, check_path_rows, spread_rows
 
 pytestmark = pytest.mark.gpu
 
 
-def make_step(nsa, w):
+def make_step(nsa, w, hint=1):
     T = w.num_rows
     md = nsa.new_metadata_buffers(w.mode, w.bs, T, w.max_seqlen_k, DEV)
     logits = torch.empty(T, nsa.logits_row_stride(w.max_seqlen_k),
@@ -42,7 +45,8 @@ def make_step(nsa, w):
         nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
                                md["real_page_table"], md["token_to_req"],
                                md["seqlens_expanded"], w.max_seqlen_k,
-                               logits=logits, dtype=idx_dtype(nsa, w), key_hist=kh)
+                               logits=logits, dtype=idx_dtype(nsa, w), key_hist=kh,
+                               rows_per_request=hint)
         nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                w.max_seqlen_k, table=md["real_page_table"],
                                token_to_req=md["token_to_req"], out=slots,
@@ -61,7 +65,13 @@ def make_step(nsa, w):
         out.fill_(3.0)
         lse.fill_(-1.0)
 
-    return step, snapshot, scribble
+    def against_oracle(what):
+        rows = spread_rows(w, 12)
+        err, _ = check_path_rows(w, md, logits, None, slots, cache, out, lse, rows,
+                                 check_cache=False)
+        note(f"  {what}: {len(rows)} rows match the oracle (max logit error {err:.2e})")
+
+    return step, snapshot, scribble, against_oracle
 
 
 def assert_same(got, want, what):
@@ -72,19 +82,22 @@ def assert_same(got, want, what):
             assert got[k] == want[k], f"{what}: {k} {got[k]} != {want[k]}"
 
 
-@pytest.mark.parametrize("name,overrides", [
-    ("decode_b32", {}),
-    ("verify", dict(bs=8, seqlen_range=(16384, 32768))),
+@pytest.mark.parametrize("name,overrides,hint", [
+    ("decode_b32", {}, 1),
+    ("verify", dict(bs=8, seqlen_range=(16384, 32768)), 1),
+    # the verify launch of the benchmark: four rows per indexer block
+    ("verify", dict(bs=8, seqlen_range=(16384, 32768)), 4),
 ])
-def test_step_graph_replays_match_eager(name, overrides):
+def test_step_graph_replays_match_eager_and_oracle(name, overrides, hint):
     nsa = need_gpu()
     w = W.make_workload(name, device=DEV, **overrides)
-    note(f"graph: {name} T={w.num_rows} H={w.heads} kv={w.kv_kind}")
-    step, snapshot, scribble = make_step(nsa, w)
+    note(f"graph: {name} T={w.num_rows} H={w.heads} kv={w.kv_kind} hint={hint}")
+    step, snapshot, scribble, against_oracle = make_step(nsa, w, hint)
     step()
     torch.cuda.synchronize()
     ref = snapshot()
     assert ref["key_hist_sum"] == 0
+    against_oracle("eager step")
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -103,6 +116,7 @@ def test_step_graph_replays_match_eager(name, overrides):
         g.replay()
         torch.cuda.synchronize()
         assert_same(snapshot(), ref, f"{name} replay {rep}")
+        against_oracle(f"replay {rep}")
         step()                      # eager step between replays
         torch.cuda.synchronize()
 
@@ -114,9 +128,11 @@ def test_step_graph_replays_match_eager(name, overrides):
     torch.cuda.synchronize()
     ref2 = snapshot()
     assert not torch.equal(ref2["seqlens_expanded"], ref["seqlens_expanded"])
+    against_oracle("eager step after the refresh")
     for rep in range(2):
         scribble()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert_same(snapshot(), ref2, f"{name} refreshed replay {rep}")
+        against_oracle(f"refreshed replay {rep}")
