@@ -360,6 +360,23 @@ int nsa_sparse_mla_extend(const void* q, int64_t q_tok_stride,
                           void* out, float* lse, void* workspace,
                           size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as nsa_sparse_mla_decode, with its split workspace taken from a
+ * fixed device array inside the library (64 MiB, one per GPU, held until the
+ * process ends; its device address is looked up once per device). Nothing is
+ * allocated. A shape whose plan needs more scratch than that returns
+ * NSA_ERR_WORKSPACE. Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (on different streams) race and must be serialised by
+ * the caller. Arguments and results as nsa_sparse_mla_decode. */
+int nsa_sparse_mla_decode_noalloc(const void* q, int64_t q_tok_stride,
+                                  int64_t q_head_stride, const void* kv_cache,
+                                  int kv_dtype, int64_t num_slots,
+                                  const int32_t* indices, int64_t idx_stride,
+                                  const int32_t* nsa_cache_seqlens, int T, int H,
+                                  int topk, int d_qk, int d_v, float sm_scale,
+                                  void* out, float* lse, void* stream);
+
 /* ---- a6: fp8 block-scaled latent cache --------------------------------------------
  * [nsa-fork] _forward_flashmla_decode and [dsa-main] _forward_flashmla_kv
  * call quantize_k_cache(kv_cache) to produce the fp8 cache the decode kernel

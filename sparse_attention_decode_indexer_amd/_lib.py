@@ -42,6 +42,9 @@ SIGNATURES = {
     "nsa_sparse_mla_extend": (c_int, [
         P, c_i64, c_i64, P, c_int, c_i64, P, c_i64, P, c_int, c_int, c_int,
         c_int, c_int, c_f32, P, P, P, c_size, P]),
+    "nsa_sparse_mla_decode_noalloc": (c_int, [
+        P, c_i64, c_i64, P, c_int, c_i64, P, c_i64, P, c_int, c_int, c_int,
+        c_int, c_int, c_f32, P, P, P]),
     "nsa_quantize_k_cache": (c_int, [P, c_i64, c_i64, P, P]),
     "nsa_set_mla_kv_buffer": (c_int, [P, c_i64, P, c_i64, P, c_int, P, c_int,
                                       c_i64, P]),

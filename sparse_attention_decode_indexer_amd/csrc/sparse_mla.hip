@@ -34,6 +34,8 @@
 //     kernel merges them in split order (bit-reproducible).
 #include "common.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -1042,7 +1044,63 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
   return nsa::check_launch(fn);
 }
 
+// ---- allocation-free variant: the workspace is a file-scope device array
+// (one copy per GPU, allocated when the code object loads). Host code never
+// passes the array's name to a kernel: its device address comes from
+// hipGetSymbolAddress, taken once per device and cached.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(const char* fn, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  NSA_REQUIRE(e == hipSuccess, NSA_ERR_LAUNCH, "%s: hipGetDevice: %s", fn,
+              hipGetErrorString(e));
+  NSA_REQUIRE(dev >= 0 && dev < kMaxDevices, NSA_ERR_UNSUPPORTED,
+              "%s: device %d >= %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    NSA_REQUIRE(e == hipSuccess && p != nullptr, NSA_ERR_LAUNCH,
+                "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return NSA_OK;
+}
+
 }  // namespace
+
+extern "C" int nsa_sparse_mla_decode_noalloc(
+    const void* q, int64_t q_tok_stride, int64_t q_head_stride,
+    const void* kv_cache, int kv_dtype, int64_t num_slots,
+    const int32_t* indices, int64_t idx_stride,
+    const int32_t* nsa_cache_seqlens, int T, int H, int topk, int d_qk,
+    int d_v, float sm_scale, void* out, float* lse, void* stream) {
+  const char* fn = "nsa_sparse_mla_decode_noalloc";
+  int st = check_args(fn, q, q_tok_stride, q_head_stride, kv_cache, kv_dtype,
+                      num_slots, indices, idx_stride, T, H, topk, d_qk, d_v, out);
+  if (st != NSA_OK) return st;
+  if (T == 0) return nsa::ok();
+  const size_t need =
+      workspace_bytes(make_plan(T, H, topk, true, kv_dtype == NSA_KV_FP8_656), T, H);
+  NSA_REQUIRE(need <= kScratchBytes, NSA_ERR_WORKSPACE,
+              "%s: this shape needs %zu bytes of scratch, the static array holds %zu",
+              fn, need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_current_device(fn, &ws);
+    if (st != NSA_OK) return st;
+  }
+  return run(fn, true, q, q_tok_stride, q_head_stride, kv_cache, kv_dtype,
+             num_slots, indices, idx_stride, nsa_cache_seqlens, T, H, topk, d_qk,
+             d_v, sm_scale, out, lse, ws, ws ? kScratchBytes : 0, stream);
+}
 
 extern "C" int nsa_sparse_mla_workspace_size(int T, int H, int topk, int d_v,
                                              size_t* bytes) {
