@@ -285,12 +285,14 @@ def test_sparse_mla_strided_q_and_determinism():
     check_attention(a.float().cpu().numpy(), la.cpu().numpy(), o_ref, lse_ref, "bf16")
 
 
-def test_sparse_mla_score_jump_reruns_exactly():
+@pytest.mark.parametrize("H", [64, 128])
+def test_sparse_mla_score_jump_reruns_exactly(H):
     """Scores of a later step far above the first step's (exp2 of the scaled
-    difference, about 332, overflows fp32): the 64-head fp8 kernel must
-    still match the oracle (it runs the split again with the true maximum)."""
+    difference, about 332, overflows fp32): the 64-head fp8 kernel, alone
+    (H = 64) or as two head blocks (H = 128), must still match the oracle (it
+    runs the split again with the true maximum)."""
     nsa = need_gpu()
-    T, H, topk = 2, 64, 64
+    T, topk = 2, 64
     q = torch.ones(T, H, 576, dtype=torch.bfloat16)
     kv = torch.zeros(64, 576, dtype=torch.bfloat16)
     kv[32:] = 0.1                                    # second step: q.k = 57.6
@@ -307,3 +309,44 @@ def test_sparse_mla_score_jump_reruns_exactly():
                                                   CacheFromRows(dict(enumerate(vals))),
                                                   idx, 4.0)
     check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "fp8")
+
+
+@pytest.mark.parametrize("T,topk", [(5, 2048), (256, 256), (3, 100)])
+def test_sparse_mla_128_heads_fp8_edges_and_determinism(T, topk):
+    """128 heads over an fp8 cache (two 64-head blocks per row): KV splits
+    (few rows) or none (T = 256), index rows with nsa_cache_seqlens cuts, an
+    empty row, a one-slot row and out-of-range slots; two calls on one
+    workspace give bit-identical results (splits are merged in split
+    order)."""
+    nsa = need_gpu()
+    rng = np.random.default_rng(T + topk)
+    H, S = 128, 4000
+    q, cache, vals, idx = _random_case(rng, T, H, topk, S, "fp8", frac_pad=0.2)
+    idx[0, :] = -1                                   # empty row
+    idx[1, 1:] = -1                                  # one slot
+    idx[2, 3] = S + 11                               # out of range: ignored
+    seqlens = np.full(T, topk, np.int32)
+    seqlens[2] = min(topk, 70)
+    if T > 4:
+        seqlens[4] = 0
+    idx_d = torch.as_tensor(idx, dtype=torch.int32, device=DEV)
+    sl_d = torch.as_tensor(seqlens, device=DEV)
+    ws = torch.empty(max(nsa.sparse_mla_workspace_size(T, H, topk), 16),
+                     dtype=torch.uint8, device=DEV)
+    nsa.nsa_check_device_errors()
+    a, la = nsa.nsa_sparse_mla_decode(q.to(DEV), cache, nsa.KV_FP8_656, idx_d, 0.0721,
+                                      nsa_cache_seqlens=sl_d, workspace=ws)
+    b, lb = nsa.nsa_sparse_mla_decode(q.to(DEV), cache, nsa.KV_FP8_656, idx_d, 0.0721,
+                                      nsa_cache_seqlens=sl_d, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    assert nsa.nsa_check_device_errors() == nsa.DEVERR_SLOT
+    clean = np.where((idx >= 0) & (idx < S), idx, -1)
+    o_ref, lse_ref = oracle.sparse_mla.sparse_mla(q.to(torch.float64).numpy(),
+                                                  CacheFromRows(dict(enumerate(vals))),
+                                                  clean, 0.0721, nsa_cache_seqlens=seqlens)
+    o = a.float().cpu().numpy()
+    check_attention(o, la.cpu().numpy(), o_ref, lse_ref, "fp8", what=f"128 heads T={T}")
+    assert (o[0] == 0).all() and np.isneginf(la.cpu().numpy()[0]).all()
+    np.testing.assert_allclose(o[1], np.broadcast_to(vals[idx[1, 0], :512], (H, 512)),
+                               rtol=1e-2, atol=1e-2)
