@@ -70,7 +70,7 @@ def _check_repeats(got, n0):
 
 
 @pytest.mark.parametrize("kind", KINDS)
-@pytest.mark.parametrize("topk", [256, 2048])
+@pytest.mark.parametrize("topk", [256, 2048, 8192])
 @pytest.mark.parametrize("pad", [6, 67])   # odd row stride: scalar loads; else vector
 @pytest.mark.parametrize("span", ["long", "short"])
 def test_topk_exact_on_given_logits(kind, topk, pad, span):
@@ -204,12 +204,16 @@ def _random_case(rng, T, H, topk, num_slots, kind, frac_pad=0.1):
                                       (2, 32, 100), (40, 16, 64), (4, 48, 512),
                                       # 64-head blocks: many splits, an odd last
                                       # step of a split, > 2048 slots per row
-                                      (2, 128, 300), (200, 64, 96), (1, 64, 4096)])
+                                      (2, 128, 300), (200, 64, 96), (1, 64, 4096),
+                                      # the other head counts the entry points
+                                      # take, and the largest topk (8192)
+                                      (3, 80, 160), (2, 96, 8192), (2, 112, 1000),
+                                      (1, 128, 8192)])
 def test_sparse_mla_decode(kind, T, H, topk):
     nsa = need_gpu()
     note(f"sparse_mla {kind} T={T} H={H} topk={topk}")
     rng = np.random.default_rng(T * 1000 + H + topk)
-    q, cache, vals, idx = _random_case(rng, T, H, topk, 6000, kind)
+    q, cache, vals, idx = _random_case(rng, T, H, topk, max(6000, topk + 1000), kind)
     kvd = nsa.KV_FP8_656 if kind == "fp8" else nsa.KV_BF16_576
     out, lse = nsa.nsa_sparse_mla_decode(q.to(DEV), cache, kvd,
                                          torch.as_tensor(idx, dtype=torch.int32, device=DEV),
