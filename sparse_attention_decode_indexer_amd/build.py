@@ -15,7 +15,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libnsa.so")
 
 SOURCES = ["status.cpp", "metadata.hip", "transform.hip", "topk.hip",
-           "indexer.hip", "sparse_mla.hip", "quant.hip", "ragged.hip"]
+           "indexer.hip", "sparse_mla.hip", "sparse_mla_h128.hip", "quant.hip",
+           "ragged.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -38,6 +39,9 @@ FLAGS = [
 # option is not global).
 SOURCE_FLAGS = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the 128-head attention kernel keeps its score accumulators in VGPRs and
+    # gives all 256 AGPRs to O (those MFMAs are written in their AGPR form)
+    "sparse_mla_h128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

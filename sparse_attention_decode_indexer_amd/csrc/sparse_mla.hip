@@ -7,10 +7,14 @@
 //   s_i = sm_scale * q[t,h,:576] . K_i[:576],  o = softmax(s) . K[:, :512],
 //   lse = log sum_i exp(s_i).
 //
-// Two kernels. An fp8 cache with H a multiple of 64 (the decode shape of the
-// large models) runs the 64-head kernel further below: 32x32 MFMA tiles, a
-// K tile dequantized once per step for 64 heads, software-pipelined steps.
-// Other shapes (16..48 heads, bf16 caches) run the narrower kernel:
+// Three kernels. An fp8 cache with H a multiple of 64 (the decode shape of
+// the large models) runs the 64-head kernel further below: 32x32 MFMA tiles,
+// a K tile dequantized once per step for 64 heads, software-pipelined steps.
+// With H = 128 and more rows than 128 (target-verify, draft-extend), the
+// rows alone fill the CUs and the 128-head kernel of sparse_mla_h128.hip
+// runs instead: one block per row, each gathered row dequantized once for
+// all heads. Other shapes (16..48 heads, bf16 caches) run the narrower
+// kernel:
 //
 // MI355X design of the narrower kernel (one 256-thread block = 4 waves):
 //   * a block owns one query row, HB = 16*NH*HW heads and one KV split; wave
@@ -32,53 +36,21 @@
 //   * the online softmax runs in the log2 domain in fp32;
 //   * KV splits write (o / l, lse) partials to the workspace and a second
 //     kernel merges them in split order (bit-reproducible).
-#include "common.h"
+#include "sparse_mla_shared.h"
 
 #include <mutex>
 
 namespace {
 
+using namespace nsa_mla;
+
 constexpr int kThreads = 256;
-constexpr int kStep = 32;                 // slots per step
-constexpr int kDQK = 576, kDV = 512;
-constexpr int kKsStride = kDQK + 8;       // bf16 elements per staged K row
-constexpr int kKsRow = kKsStride * 2;     // bytes per staged K row (1168)
-constexpr int kKsBytes = kStep * kKsRow;  // 37376
 constexpr int kKSteps = kDQK / 32;        // 18 contraction steps of 32 dims
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;             // log2 headroom before O is rescaled
 
-struct Params {
-  const uint16_t* q;
-  int64_t q_tok_stride, q_head_stride;
-  const uint8_t* kv;
-  int64_t num_slots;
-  const int32_t* idx;
-  int64_t idx_stride;
-  const int32_t* seqlens;  // nullable
-  int T, H, topk;
-  float scale_log2;
-  uint16_t* out;
-  float* lse;              // nullable
-  float* ws_o;             // [n_splits][T][H][512] when n_splits > 1
-  float* ws_lse;           // [n_splits][T][H]
-  int n_splits, split_slots, n_hb;
-};
 
-__device__ __forceinline__ uint32_t xcd_logical_block(uint32_t bid, uint32_t n) {
-  const uint32_t q = n / 8, r = n % 8, x = bid % 8;
-  return x * q + (x < r ? x : r) + bid / 8;
-}
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// 4 bf16 of one value dim across 4 slot rows (see the design note above).
-__device__ __forceinline__ v4i16 read_tr(const uint8_t* lds_byte_addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16*)(__attribute__((address_space(3))) uint8_t*)lds_byte_addr);
-}
 
 // Prefetch registers of one thread for one step. Loads are branch-free: an
 // absent slot (-1) reads slot 0 and its values are zeroed when staged, so no
@@ -514,10 +486,8 @@ sparse_mla_kernel(const Params p) {
 // register stages that alternate (the loop is unrolled by two, so no
 // register copy waits on a load in flight).
 constexpr int kThreadsW = 256;
-constexpr int kMaxSplit = 2048;                // slots per block
 constexpr int kIdsCap = 10 * kThreadsW;        // 2560 >= kMaxSplit + 5 steps of overrun
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Gather registers of one thread for one step: slot qd = tid / 8, 16-byte
 // code chunks cc + 8k (k = 0..3, chunk k lies in 128-block k), the slot's 4
@@ -918,6 +888,7 @@ combine_splits_kernel(const float* __restrict__ ws_o,
 }
 
 struct Plan {
+  bool h128;   // all 128 heads per block (sparse_mla_h128_kernel)
   bool wide;   // 64 heads per block (sparse_mla_h64_kernel)
   int nh, hw, hb_heads, n_hb, n_splits, split_slots;
 };
@@ -927,6 +898,15 @@ struct Plan {
 // slots per block; the narrower kernel runs two blocks per CU.
 Plan make_plan(int T, int H, int topk, bool decode, bool fp8) {
   Plan pl;
+  // one 128-head block per row when the rows alone fill the CUs: more work
+  // per second than two 64-head blocks per row (each gathered row is
+  // dequantised once), and no KV splits to merge
+  pl.h128 = fp8 && H == 128 && T > 128 && topk <= kMaxSplit;
+  if (pl.h128) {
+    pl.wide = false; pl.nh = 1; pl.hw = 1; pl.hb_heads = 128; pl.n_hb = 1;
+    pl.n_splits = 1; pl.split_slots = (topk + kStep - 1) / kStep * kStep;
+    return pl;
+  }
   pl.wide = fp8 && H % 64 == 0;
   if (pl.wide) { pl.nh = 1; pl.hw = 4; }
   else if (H % 32 == 0) { pl.nh = 1; pl.hw = 2; }
@@ -1028,7 +1008,9 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
     if (fp8) hipLaunchKernelGGL((sparse_mla_kernel<NH, HW, true>), grid, block, 0, s, p); \
     else hipLaunchKernelGGL((sparse_mla_kernel<NH, HW, false>), grid, block, 0, s, p);    \
   } while (0)
-  if (pl.wide) {
+  if (pl.h128) {
+    launch_sparse_mla_h128(p, (unsigned)blocks, s);
+  } else if (pl.wide) {
     hipLaunchKernelGGL(sparse_mla_h64_kernel, grid, block, 0, s, p);
   } else if (pl.hw == 2) {
     NSA_MLA_LAUNCH(1, 2);

@@ -289,14 +289,15 @@ def test_sparse_mla_strided_q_and_determinism():
     check_attention(a.float().cpu().numpy(), la.cpu().numpy(), o_ref, lse_ref, "bf16")
 
 
-@pytest.mark.parametrize("H", [64, 128])
-def test_sparse_mla_score_jump_reruns_exactly(H):
+@pytest.mark.parametrize("H,T", [(64, 2), (128, 2), (128, 130)])
+def test_sparse_mla_score_jump_reruns_exactly(H, T):
     """Scores of a later step far above the first step's (exp2 of the scaled
     difference, about 332, overflows fp32): the 64-head fp8 kernel, alone
-    (H = 64) or as two head blocks (H = 128), must still match the oracle (it
-    runs the split again with the true maximum)."""
+    (H = 64) or as two head blocks (H = 128), and the 128-head kernel (more
+    than 128 rows) must still match the oracle (they run the split or row
+    again with the true maximum)."""
     nsa = need_gpu()
-    T, topk = 2, 64
+    topk = 64
     q = torch.ones(T, H, 576, dtype=torch.bfloat16)
     kv = torch.zeros(64, 576, dtype=torch.bfloat16)
     kv[32:] = 0.1                                    # second step: q.k = 57.6
@@ -304,7 +305,7 @@ def test_sparse_mla_score_jump_reruns_exactly(H):
     raw = oracle.quant.quantize_k_cache(bits)
     vals = oracle.quant.dequantize_rows(raw)
     idx = np.tile(np.arange(64), (T, 1))
-    idx[1] = idx[1][::-1]                            # large scores first
+    idx[1::2] = idx[1::2, ::-1]                      # large scores first
     out, lse = nsa.nsa_sparse_mla_decode(q.to(DEV), torch.as_tensor(raw, device=DEV),
                                          nsa.KV_FP8_656,
                                          torch.as_tensor(idx, dtype=torch.int32, device=DEV),
@@ -315,13 +316,15 @@ def test_sparse_mla_score_jump_reruns_exactly(H):
     check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "fp8")
 
 
-@pytest.mark.parametrize("T,topk", [(5, 2048), (256, 256), (3, 100)])
+@pytest.mark.parametrize("T,topk", [(5, 2048), (3, 100), (128, 160),
+                                    # more than 128 rows: one 128-head block per row
+                                    (129, 2048), (200, 300), (256, 256), (300, 64)])
 def test_sparse_mla_128_heads_fp8_edges_and_determinism(T, topk):
-    """128 heads over an fp8 cache (two 64-head blocks per row): KV splits
-    (few rows) or none (T = 256), index rows with nsa_cache_seqlens cuts, an
-    empty row, a one-slot row and out-of-range slots; two calls on one
-    workspace give bit-identical results (splits are merged in split
-    order)."""
+    """128 heads over an fp8 cache: up to 128 rows, two 64-head blocks per
+    row with KV splits when the rows are few; above 128 rows, one 128-head
+    block per row. Index rows with nsa_cache_seqlens cuts, an empty row, a
+    one-slot row and out-of-range slots; two calls on one workspace give
+    bit-identical results (splits are merged in split order)."""
     nsa = need_gpu()
     rng = np.random.default_rng(T + topk)
     H, S = 128, 4000
