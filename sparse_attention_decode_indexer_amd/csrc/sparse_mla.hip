@@ -7,14 +7,14 @@
 //   s_i = sm_scale * q[t,h,:576] . K_i[:576],  o = softmax(s) . K[:, :512],
 //   lse = log sum_i exp(s_i).
 //
-// Three kernels. An fp8 cache with H a multiple of 64 (the decode shape of
-// the large models) runs the 64-head kernel further below: 32x32 MFMA tiles,
-// a K tile dequantized once per step for 64 heads, software-pipelined steps.
-// With H = 128 and more rows than 128 (target-verify, draft-extend), the
-// rows alone fill the CUs and the 128-head kernel of sparse_mla_h128.hip
-// runs instead: one block per row, each gathered row dequantized once for
-// all heads. Other shapes (16..48 heads, bf16 caches) run the narrower
-// kernel:
+// Three kernels. An fp8 cache with H = 128 (the decode shape of the large
+// models) runs the 128-head kernel of sparse_mla_h128.hip: one block per
+// (row, KV split), each gathered row dequantized once for all heads, splits
+// merged from bf16 partials. An fp8 cache with H = 64 (or shapes the
+// 128-head plan does not take) runs the 64-head kernel further below: 32x32
+// MFMA tiles, a K tile dequantized once per step for 64 heads,
+// software-pipelined steps. Other shapes (16..48 heads, bf16 caches) run the
+// narrower kernel:
 //
 // MI355X design of the narrower kernel (one 256-thread block = 4 waves):
 //   * a block owns one query row, HB = 16*NH*HW heads and one KV split; wave
@@ -851,9 +851,11 @@ sparse_mla_h64_kernel(const Params p) {
   }
 }
 
-// Merge of KV-split partials, in split order: one wave per (row, head).
+// Merge of KV-split partials, in split order: one wave per (row, head). PT:
+// float rows (the 16..64-head kernels) or bf16 rows (the 128-head kernel).
+template <typename PT>
 __global__ void __launch_bounds__(256)
-combine_splits_kernel(const float* __restrict__ ws_o,
+combine_splits_kernel(const PT* __restrict__ ws_o,
                       const float* __restrict__ ws_lse, int T, int H,
                       int n_splits, uint16_t* __restrict__ out,
                       float* __restrict__ lse) {
@@ -870,8 +872,17 @@ combine_splits_kernel(const float* __restrict__ ws_o,
       const float ls = ws_lse[s * TH + th];
       const float wgt = ls == -INFINITY ? 0.0f : __expf(ls - mx);
       den += wgt;
-      const float4* src = reinterpret_cast<const float4*>(ws_o + (s * TH + th) * kDV + lane * 8);
-      const float4 a = src[0], b = src[1];
+      float4 a, b;
+      if constexpr (sizeof(PT) == 4) {
+        const float4* src = reinterpret_cast<const float4*>(ws_o + (s * TH + th) * kDV + lane * 8);
+        a = src[0]; b = src[1];
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(ws_o + (s * TH + th) * kDV + lane * 8);
+        a = make_float4(bf16_bits_to_f32(u.x & 0xFFFFu), bf16_bits_to_f32(u.x >> 16),
+                        bf16_bits_to_f32(u.y & 0xFFFFu), bf16_bits_to_f32(u.y >> 16));
+        b = make_float4(bf16_bits_to_f32(u.z & 0xFFFFu), bf16_bits_to_f32(u.z >> 16),
+                        bf16_bits_to_f32(u.w & 0xFFFFu), bf16_bits_to_f32(u.w >> 16));
+      }
       acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
       acc[4] += wgt * b.x; acc[5] += wgt * b.y; acc[6] += wgt * b.z; acc[7] += wgt * b.w;
     }
@@ -887,6 +898,48 @@ combine_splits_kernel(const float* __restrict__ ws_o,
   if (lse && lane == 0) lse[th] = den > 0.0f ? mx + __logf(den) : -INFINITY;
 }
 
+// Merge of the 128-head kernel's KV-split partials (bf16 rows o_s / l_s and
+// lse_s), NS splits known at compile time so that every load of a (row,
+// head) is issued before any is used; in split order as above.
+template <int NS>
+__global__ void __launch_bounds__(256)
+combine_bf16_kernel(const uint16_t* __restrict__ ws_o, const float* __restrict__ ws_lse,
+                    int T, int H, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (th >= (int64_t)T * H) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t TH = (int64_t)T * H;
+  float ls[NS];
+  uint4 u[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    ls[s] = ws_lse[s * TH + th];
+    u[s] = *reinterpret_cast<const uint4*>(ws_o + (s * TH + th) * kDV + lane * 8);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) mx = fmaxf(mx, ls[s]);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float den = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float wgt = (mx == -INFINITY || ls[s] == -INFINITY) ? 0.0f : __expf(ls[s] - mx);
+    den += wgt;
+    const uint32_t w[4] = {u[s].x, u[s].y, u[s].z, u[s].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wgt * bf16_bits_to_f32(w[i] & 0xFFFFu);
+      acc[2 * i + 1] += wgt * bf16_bits_to_f32(w[i] >> 16);
+    }
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *reinterpret_cast<uint4*>(out + th * kDV + lane * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  if (lse && lane == 0) lse[th] = den > 0.0f ? mx + __logf(den) : -INFINITY;
+}
+
 struct Plan {
   bool h128;   // all 128 heads per block (sparse_mla_h128_kernel)
   bool wide;   // 64 heads per block (sparse_mla_h64_kernel)
@@ -898,14 +951,27 @@ struct Plan {
 // slots per block; the narrower kernel runs two blocks per CU.
 Plan make_plan(int T, int H, int topk, bool decode, bool fp8) {
   Plan pl;
-  // one 128-head block per row when the rows alone fill the CUs: more work
-  // per second than two 64-head blocks per row (each gathered row is
-  // dequantised once), and no KV splits to merge
-  pl.h128 = fp8 && H == 128 && T > 128 && topk <= kMaxSplit;
+  // 128 heads over an fp8 cache: the 128-head kernel does more work per
+  // second than two 64-head blocks per row (each gathered row is dequantised
+  // once for all heads). More than 128 rows fill the CUs with one block per
+  // row; fewer rows are split over KV (about 256 blocks, at least 128 slots
+  // per split, at most kMaxSplit) and merged by combine_bf16_kernel. Shapes
+  // it cannot split that way (tiny topk, topk > 2 kMaxSplit) take the
+  // 64-head kernel.
+  pl.h128 = fp8 && H == 128 && topk <= 2 * kMaxSplit;
   if (pl.h128) {
     pl.wide = false; pl.nh = 1; pl.hw = 1; pl.hb_heads = 128; pl.n_hb = 1;
-    pl.n_splits = 1; pl.split_slots = (topk + kStep - 1) / kStep * kStep;
-    return pl;
+    int ns = T > 128 ? 1 : (int)((256 + T - 1) / T);
+    const int mx = (topk + 127) / 128;
+    ns = ns > mx ? mx : ns;
+    int ss = (topk + ns - 1) / ns;
+    ss = (ss + kStep - 1) / kStep * kStep;
+    ns = (topk + ss - 1) / ss;
+    if (ss <= kMaxSplit && (T > 128 || ns > 1)) {
+      pl.n_splits = ns; pl.split_slots = ss;
+      return pl;
+    }
+    pl.h128 = false;
   }
   pl.wide = fp8 && H % 64 == 0;
   if (pl.wide) { pl.nh = 1; pl.hw = 4; }
@@ -931,6 +997,8 @@ Plan make_plan(int T, int H, int topk, bool decode, bool fp8) {
 
 size_t workspace_bytes(const Plan& pl, int T, int H) {
   if (pl.n_splits <= 1) return 0;
+  if (pl.h128)   // bf16 partials + fp32 lse
+    return (size_t)pl.n_splits * T * H * (kDV * sizeof(uint16_t) + sizeof(float));
   return (size_t)pl.n_splits * T * H * (kDV + 1) * sizeof(float);
 }
 
@@ -994,7 +1062,9 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
   p.lse = lse;
   p.ws_o = pl.n_splits > 1 ? static_cast<float*>(workspace) : nullptr;
   p.ws_lse = pl.n_splits > 1
-                 ? static_cast<float*>(workspace) + (size_t)pl.n_splits * T * H * kDV
+                 ? (pl.h128 ? reinterpret_cast<float*>(static_cast<uint16_t*>(workspace) +
+                                                       (size_t)pl.n_splits * T * H * kDV)
+                            : static_cast<float*>(workspace) + (size_t)pl.n_splits * T * H * kDV)
                  : nullptr;
   p.n_splits = pl.n_splits;
   p.split_slots = pl.split_slots;
@@ -1021,8 +1091,19 @@ int run(const char* fn, bool decode, const void* q, int64_t q_tok_stride,
   st = nsa::check_launch(fn);
   if (st != NSA_OK || pl.n_splits == 1) return st;
   const int64_t cb = ((int64_t)T * H + 3) / 4;
-  hipLaunchKernelGGL(combine_splits_kernel, dim3((unsigned)cb), dim3(256), 0, s,
-                     p.ws_o, p.ws_lse, T, H, pl.n_splits, p.out, lse);
+  const uint16_t* wsb = reinterpret_cast<const uint16_t*>(p.ws_o);
+  if (pl.h128 && pl.n_splits == 2)
+    hipLaunchKernelGGL(combine_bf16_kernel<2>, dim3((unsigned)cb), dim3(256), 0, s, wsb,
+                       p.ws_lse, T, H, p.out, lse);
+  else if (pl.h128 && pl.n_splits == 4)
+    hipLaunchKernelGGL(combine_bf16_kernel<4>, dim3((unsigned)cb), dim3(256), 0, s, wsb,
+                       p.ws_lse, T, H, p.out, lse);
+  else if (pl.h128)
+    hipLaunchKernelGGL(combine_splits_kernel<uint16_t>, dim3((unsigned)cb), dim3(256), 0, s,
+                       wsb, p.ws_lse, T, H, pl.n_splits, p.out, lse);
+  else
+    hipLaunchKernelGGL(combine_splits_kernel<float>, dim3((unsigned)cb), dim3(256), 0, s,
+                       p.ws_o, p.ws_lse, T, H, pl.n_splits, p.out, lse);
   return nsa::check_launch(fn);
 }
 

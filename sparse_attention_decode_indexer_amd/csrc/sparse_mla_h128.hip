@@ -12,15 +12,14 @@ namespace nsa_mla {
 namespace {
 
 // ---- 128-head kernel (fp8 cache, H = 128) ----------------------------------
-// A block owns one query row and all 128 heads, so each gathered fp8 row is
-// dequantised once per row (the 64-head kernel of sparse_mla.hip does it once
-// per 64-head block, two blocks per row). The plan runs it when the rows
-// alone fill the CUs (more than 128 rows: target-verify, draft-extend), one
-// block per row and no KV splits; with fewer rows the 64-head kernel's two
-// blocks per row (and splits) keep more CUs busy. Wave w owns heads
-// 32w .. 32w+31 and, for them, the whole 576-wide contraction and all 512
-// value dims: no partial scores are exchanged between waves and each softmax
-// runs once. Q (36 bf16x8 B operands) stays in VGPRs, the O^T accumulators
+// A block owns one query row, all 128 heads and one KV split, so each
+// gathered fp8 row is dequantised once for all heads (the 64-head kernel of
+// sparse_mla.hip does it once per 64-head block, two blocks per row). More
+// than 128 rows (target-verify, draft-extend) take one block per row; fewer
+// rows are split over KV so that about 256 blocks fill the CUs. Wave w owns
+// heads 32w .. 32w+31 and, for them, the whole 576-wide contraction and all
+// 512 value dims: no partial scores are exchanged between waves and each
+// softmax runs once. Q (36 bf16x8 B operands) stays in VGPRs, the O^T accumulators
 // (16 tiles of 32 value dims x 32 heads) in AGPRs.
 //   * S^T = K.Q^T with v_mfma_f32_32x32x16_bf16: A = 32 slots x 16 dims of
 //     the bf16 K tile (LDS), B = Q^T; lane (head c32, half kg) receives the
@@ -45,7 +44,9 @@ namespace {
 //     first step with a valid slot), exponents clamped, an exact re-run of the
 //     row when a later score exceeds the reference by more than 2^64;
 //   * output: each wave stages its heads' rows (bf16, divided by l) in LDS
-//     and writes each head's 1 KB row with one coalesced store.
+//     and writes each head's 1 KB row with one coalesced store, into the
+//     output (one split) or into the workspace as the split's partial, with
+//     its log-sum-exp, for the merge kernel of sparse_mla.hip.
 constexpr int kW128Slots = 8;                               // rows per wave and step
 constexpr int kRawRow = 656;
 constexpr int kRawWave = kW128Slots * kRawRow;              // 5248
@@ -109,19 +110,24 @@ sparse_mla_h128_kernel(const Params p) {
   const int grp = lane >> 4, sl = lane & 15;
   const int h = wave * 32 + c32;                       // this lane's head
 
-  // one block per query row (the host guarantees topk <= kMaxSplit)
-  const int64_t t = xcd_logical_block(blockIdx.x, gridDim.x);
+  // one block per (query row, KV split); the plan keeps split_slots <=
+  // kMaxSplit
+  const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int split = lb % p.n_splits;
+  const int64_t t = lb / p.n_splits;
 
-  int n = p.num_slots > 0 ? p.topk : 0;
+  int n_row = p.num_slots > 0 ? p.topk : 0;
   if (p.seqlens) {
     const int sl_ = p.seqlens[t];
-    n = sl_ < 0 ? 0 : (sl_ < n ? sl_ : n);
+    n_row = sl_ < 0 ? 0 : (sl_ < n_row ? sl_ : n_row);
   }
+  const int s_begin = split * p.split_slots;
+  const int n = min(s_begin + p.split_slots, n_row) - s_begin;   // may be <= 0
   const int nsteps = n > 0 ? (n + kStep - 1) / kStep : 0;
 
   // ---- slot ids of the row (validated; -1 past its end and for bad ids)
   {
-    const int32_t* irow = p.idx + t * p.idx_stride;
+    const int32_t* irow = p.idx + t * p.idx_stride + s_begin;
     const int last = n > 0 ? n - 1 : 0;
     constexpr int kPer = (kIds128 + 255) / 256;
     int32_t v[kPer];
@@ -460,7 +466,10 @@ sparse_mla_h128_kernel(const Params p) {
   l += __shfl_xor(l, 32);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   const float lse_val = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-  uint16_t* obase = p.out + (t * p.H + wave * 32) * kDV;
+  const bool direct = p.n_splits == 1;
+  uint16_t* obase = direct ? p.out + (t * p.H + wave * 32) * kDV
+                           : reinterpret_cast<uint16_t*>(p.ws_o) +
+                                 (((int64_t)split * p.T + t) * p.H + wave * 32) * kDV;
   __syncthreads();   // every wave is done with the tiles
   uint8_t* tw = &ks[0][0] + wave * kFinWave;   // this wave's staging rows
 #pragma unroll
@@ -482,7 +491,13 @@ sparse_mla_h128_kernel(const Params p) {
       __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tw + r * kFinRow + 16 * lane),
                                   reinterpret_cast<u32x4*>(obase + (16 * half + r) * kDV + 8 * lane));
   }
-  if (kg == 0 && p.lse) p.lse[t * p.H + h] = lse_val;
+  if (kg == 0) {
+    if (direct) {
+      if (p.lse) p.lse[t * p.H + h] = lse_val;
+    } else {
+      p.ws_lse[((int64_t)split * p.T + t) * p.H + h] = lse_val;
+    }
+  }
 }
 
 }  // namespace

@@ -28,7 +28,8 @@ struct Params {
   float scale_log2;
   uint16_t* out;
   float* lse;              // nullable
-  float* ws_o;             // split partials (layout per kernel) when n_splits > 1
+  float* ws_o;             // split partials when n_splits > 1 (fp32 rows; bf16 rows for
+                           // the 128-head kernel)
   float* ws_lse;           // [n_splits][T][H]
   int n_splits, split_slots, n_hb;
 };
@@ -54,8 +55,10 @@ __device__ __forceinline__ v4i16 read_tr(const uint8_t* lds_byte_addr) {
       (lds_v4i16*)(__attribute__((address_space(3))) uint8_t*)lds_byte_addr);
 }
 
-// 128-head kernel (sparse_mla_h128.hip): one block per query row, no KV
-// splits (p.n_splits == 1, p.split_slots >= the row's slots, topk <= kMaxSplit).
+// 128-head kernel (sparse_mla_h128.hip): one block per (query row, KV split),
+// blocks = T * n_splits, p.split_slots <= kMaxSplit. With n_splits > 1 each
+// block writes its split's bf16 partial rows to p.ws_o (as uint16,
+// [n_splits][T][128][512]) and its log-sum-exp to p.ws_lse.
 int launch_sparse_mla_h128(const Params& p, unsigned blocks, hipStream_t s);
 
 }  // namespace nsa_mla

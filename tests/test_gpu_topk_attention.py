@@ -316,21 +316,24 @@ def test_sparse_mla_score_jump_reruns_exactly(H, T):
     check_attention(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "fp8")
 
 
-@pytest.mark.parametrize("T,topk", [(5, 2048), (3, 100), (128, 160),
+@pytest.mark.parametrize("T,topk", [(5, 2048), (3, 100), (128, 160), (64, 2048),
                                     # more than 128 rows: one 128-head block per row
                                     (129, 2048), (200, 300), (256, 256), (300, 64)])
 def test_sparse_mla_128_heads_fp8_edges_and_determinism(T, topk):
-    """128 heads over an fp8 cache: up to 128 rows, two 64-head blocks per
-    row with KV splits when the rows are few; above 128 rows, one 128-head
-    block per row. Index rows with nsa_cache_seqlens cuts, an empty row, a
-    one-slot row and out-of-range slots; two calls on one workspace give
-    bit-identical results (splits are merged in split order)."""
+    """128 heads over an fp8 cache, the 128-head kernel: up to 128 rows
+    split over KV (2 splits at 128 rows, 4 at 64, 16 at 5; merged from bf16
+    partials), above 128 rows one block per row; a tiny topk (3 rows, 100
+    slots) takes the 64-head kernel. Index rows with nsa_cache_seqlens cuts,
+    an empty row, a one-slot row and out-of-range slots; two calls on one
+    workspace give bit-identical results (splits are merged in split
+    order)."""
     nsa = need_gpu()
     rng = np.random.default_rng(T + topk)
     H, S = 128, 4000
     q, cache, vals, idx = _random_case(rng, T, H, topk, S, "fp8", frac_pad=0.2)
     idx[0, :] = -1                                   # empty row
-    idx[1, 1:] = -1                                  # one slot
+    idx[1, 1:] = -1                                  # one slot (row 1 is shuffled
+    idx[1, 0] = 17                                   # by _random_case: set it)
     idx[2, 3] = S + 11                               # out of range: ignored
     seqlens = np.full(T, topk, np.int32)
     seqlens[2] = min(topk, 70)

@@ -42,7 +42,7 @@ def _slots(nsa, w):
 
 @pytest.mark.parametrize("name,big,small", [
     ("decode_b32", 24, 5),        # 16 heads, bf16 cache: the narrow kernel, KV splits
-    ("decode_b128", 6, 2),        # 128 heads, fp8 cache: the 64-head kernel, KV splits
+    ("decode_b128", 6, 2),        # 128 heads, fp8 cache: the 128-head kernel, KV splits
 ])
 def test_noalloc_matches_caller_workspace_twice(name, big, small):
     nsa = need_gpu()
