@@ -31,15 +31,18 @@ namespace {
 //     normalisation needs no shuffle and the output is written in 8-byte runs;
 //   * gather: each wave loads the 656-byte rows of its 8 slots of a step with
 //     16-byte direct global->LDS loads (no staging registers; one instruction
-//     per row, lanes 0..40, the slot id a wave-uniform scalar), two steps
-//     ahead, into a raw buffer of its own; the same wave then dequantises
-//     those rows (bf16(code * block scale), round to nearest even) into the
-//     step's K tile, so waiting on its own loads is enough and the step needs
-//     one barrier;
-//   * pipeline (iteration k): the loads of step k+2, the softmax of step k-1
-//     and the dequantisation of step k+1 are spread between the 36 MFMAs of
-//     S^T(k) and the 32 of O^T += V^T(k-1).P^T(k-1); three K tiles, two raw
-//     buffers, scores double-buffered in registers;
+//     per row, lanes 0..40, the slot id a wave-uniform scalar) into a raw
+//     buffer of its own, about two iterations before it dequantises them
+//     (bf16(code * block scale), round to nearest even) into the step's K
+//     tile, so waiting on its own loads is enough and the step needs one
+//     barrier;
+//   * pipeline (iteration k): the dequantisation of step k+1 and then the
+//     loads of step k+3 into the same raw buffer, and the softmax of step k,
+//     are cut into small stages spread over the 36 MFMAs of S^T(k) and the 32
+//     of O^T += V^T(k-1).P^T(k-1), each MFMA covering about as much VALU work
+//     as the SIMD issues while it runs (with one wave per SIMD a wave's VALU
+//     instructions run under its own MFMAs only when they do not wait on each
+//     other); three K tiles, two raw buffers, P double-buffered in registers;
 //   * softmax as in the 64-head kernel: a fixed per-head reference max (the
 //     first step with a valid slot), exponents clamped, an exact re-run of the
 //     row when a later score exceeds the reference by more than 2^64;
@@ -91,10 +94,32 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* src, uint32_t lds_addr)
                : "memory");
 }
 
+// The same load of one 656-byte row, lanes 0..40, with the other lanes
+// switched off inside the asm (EXEC saved and restored there), so that the
+// code around it stays one basic block: the compiler does not move work
+// between basic blocks of the unrolled loop as it would around a branch.
+constexpr uint64_t kRowLanes = (1ull << kRowPieces) - 1;
+__device__ __forceinline__ void lds_dma_row(const uint8_t* src, uint32_t lds_addr) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(kRowLanes), "{m0}"(lds_addr)
+      : "memory");
+}
+
 __device__ __forceinline__ void wait_vm_dma() {
   // every load of this wave but the kDmaInsts most recent ones has landed
   // (the only vector-memory instructions of the loop are these row loads)
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaInsts) : "memory");
+}
+// the same with the 36 Q loads issued after the most recent row loads
+__device__ __forceinline__ void wait_vm_dma_q() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaInsts + 36) : "memory");
 }
 
 __global__ void __launch_bounds__(256, 1)
@@ -142,25 +167,34 @@ sparse_mla_h128_kernel(const Params p) {
     }
   }
 
-  // Q^T operands: lane (head c32, kg) holds dims 16i + 8kg .. +8
+  // ids visible to every wave (no wait for other loads)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+
+  // Q^T operands: lane (head c32, kg) holds dims 16i + 8kg .. +8; loaded
+  // once, behind the first row loads (the load of Q overlaps the rows'
+  // latency and the first dequantisation)
   bf16x8 qb[kQSteps];
-  {
+  static_assert(kQSteps == 36, "the prologue's wait counts 36 Q loads");
+  auto load_q = [&]() {
     const uint16_t* qh = p.q + t * p.q_tok_stride + (int64_t)h * p.q_head_stride;
 #pragma unroll
     for (int i = 0; i < kQSteps; ++i)
       qb[i] = *reinterpret_cast<const bf16x8*>(qh + 16 * i + 8 * kg);
-  }
-  __syncthreads();   // ids
+  };
 
   // ---- gather (direct to LDS) and dequantisation of this wave's 8 rows
   // row j of this wave's slots of `step`: lane i < 41 loads bytes [16i,
   // 16i+16) of the slot's 656-byte row into the wave's raw buffer
+  const uint8_t* kv_lane = p.kv + lane * 16;
   auto dma_row_id = [&](uint8_t* stage, int32_t id, int j) {
-    const uint8_t* src = p.kv + (int64_t)(id >= 0 ? id : 0) * kRawRow;
+    // the row's byte offset in scalar registers, added to the lane's base
+    uint64_t off = (uint64_t)(uint32_t)(id >= 0 ? id : 0) * kRawRow;
+    asm volatile("" : "+s"(off));
     // 32-bit LDS address arithmetic (a generic-pointer sum would be kept
     // in 64-bit registers)
     const uint32_t dst = (uint32_t)(uintptr_t)(lds_void_ptr)stage + wave * kRawWave + j * kRawRow;
-    if (lane < kRowPieces) lds_dma16(src + lane * 16, __builtin_amdgcn_readfirstlane(dst));
+    lds_dma_row(kv_lane + off, __builtin_amdgcn_readfirstlane(dst));
   };
   auto dma_row = [&](uint8_t* stage, int step, int j) {
     dma_row_id(stage, __builtin_amdgcn_readfirstlane(ids[step * kStep + wave * kW128Slots + j]), j);
@@ -169,62 +203,87 @@ sparse_mla_h128_kernel(const Params p) {
 #pragma unroll
     for (int j = 0; j < kDmaInsts; ++j) dma_row(stage, step, j);
   };
-  // the wave's row ids of `step`, read ahead into scalar registers (a read
-  // of one in front of each row load would make every load wait for all
-  // LDS reads in flight)
-  auto read_ids = [&](int32_t (&sid)[kDmaInsts], int step) {
-    const int4* ip = reinterpret_cast<const int4*>(ids + step * kStep + wave * kW128Slots);
-    const int4 a = ip[0], b = ip[1];
-    const int32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int j = 0; j < kDmaInsts; ++j) sid[j] = __builtin_amdgcn_readfirstlane(v[j]);
-  };
   // lane (sub = lane / 8, cc = lane % 8): row 8w + sub of the step, code
   // pieces cc + 8b (128-block b), rope piece cc
   const int dsub = lane >> 3, dcc = lane & 7;
   const int drow = wave * kW128Slots + dsub;
-  // A row's raw piece b (code pieces b < 4, rope piece 4) is read one group
-  // before it is stored: a read issued just before its use would make it
-  // wait for every fragment read in flight as well.
+  // Dequantisation of the wave's 8 rows of a step: 32 half-words per lane
+  // (two codes each), each in three stages: A converts the codes, B
+  // multiplies by the block scale, C rounds to bf16 (and stores the word's 4
+  // dims after its second half). Inside the loop the stages of consecutive
+  // half-words are skewed over consecutive score MFMAs (C of h-2, B of h-1
+  // and A of h together), so no stage waits on the one before it; empty asm
+  // statements pin each stage's results where they are computed.
   struct Deq {
     const uint8_t* rr;
-    u32x4 pc[5];
-    f32x4 scale;
-    bool valid;
+    u32x4 pc[2];      // raw pieces b (pc[b & 1]) and b + 1; the rope in pc[0]
+    float scale[2];   // block scales of pieces b (scale[b & 1]) and b + 1
+    int32_t id;       // the row's slot id (-1: absent)
+    float fa[2], fb[2];
+    u32x4 bf;         // bf16 pairs of the 8 dims being converted
   };
-  auto deq_fetch = [&](Deq& d, int b) {
-    d.pc[b] = *reinterpret_cast<const u32x4*>(d.rr + (b < 4 ? 16 * (dcc + 8 * b) : 528 + 16 * dcc));
+  auto deq_piece = [&](Deq& d, int b) {
+    d.pc[b & 1] = *reinterpret_cast<const u32x4*>(d.rr + (b < 4 ? 16 * (dcc + 8 * b) : 528 + 16 * dcc));
   };
   auto deq_load = [&](Deq& d, const uint8_t* stage, int step) {
     d.rr = stage + wave * kRawWave + dsub * kRawRow;
-    d.valid = ids[step * kStep + drow] >= 0;
-    d.scale = *reinterpret_cast<const f32x4*>(d.rr + 512);
-    deq_fetch(d, 0);
+    d.id = ids[step * kStep + drow];
+    d.scale[0] = *reinterpret_cast<const float*>(d.rr + 512);
+    deq_piece(d, 0);
   };
-  // piece b < 4: bf16(code * scale_b) of block b (32 bytes); piece 4: rope
-  // and the score bias. An absent slot stores zeros and a -inf bias.
-  auto deq_store = [&](const Deq& d, uint8_t* kt, float* bs, int b) {
-    if (b < 4) {
-      const u32x4 code = d.pc[b];
-      const float s = d.valid ? d.scale[b] : 0.0f;
-      const uint32_t w[4] = {code[0], code[1], code[2], code[3]};
-      uint32_t bf[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
-        bf[2 * i] = pack_bf16x2_hw(lo[0] * s, lo[1] * s);
-        bf[2 * i + 1] = pack_bf16x2_hw(hi[0] * s, hi[1] * s);
-      }
-      uint8_t* dst = kt + drow * kKsRow + 32 * (dcc + 8 * b);
-      *reinterpret_cast<uint4*>(dst) = make_uint4(bf[0], bf[1], bf[2], bf[3]);
-      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(bf[4], bf[5], bf[6], bf[7]);
+  auto deq_scale = [&](Deq& d, int b) {
+    d.scale[b & 1] = *reinterpret_cast<const float*>(d.rr + 512 + 4 * b);
+  };
+  // an absent slot's scales are 0 (applied before the block's first use)
+  auto deq_mask = [&](Deq& d, int b) { d.scale[b & 1] = d.id >= 0 ? d.scale[b & 1] : 0.0f; };
+  auto deqA = [&](Deq& d, int h) {
+    const uint32_t word = d.pc[(h >> 3) & 1][(h >> 1) & 3];
+    const auto f = (h & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true)
+                           : __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+    d.fa[0] = f[0];
+    d.fa[1] = f[1];
+    asm volatile("" : "+v"(d.fa[0]), "+v"(d.fa[1]));
+  };
+  auto deqB = [&](Deq& d, int h) {
+    const float s = d.scale[(h >> 3) & 1];
+    d.fb[0] = d.fa[0] * s;
+    d.fb[1] = d.fa[1] * s;
+    asm volatile("" : "+v"(d.fb[0]), "+v"(d.fb[1]));
+  };
+  auto deqC = [&](Deq& d, uint8_t* kt, int h) {
+    const int b = h >> 3, w = (h >> 1) & 3;
+    d.bf[h & 3] = pack_bf16x2_hw(d.fb[0], d.fb[1]);
+    if ((h & 3) == 3) {
+      uint8_t* dst = static_cast<uint8_t*>(__builtin_assume_aligned(kt, 16));
+      *reinterpret_cast<u32x4*>(dst + drow * kKsRow + 32 * (dcc + 8 * b) + 16 * (w >> 1)) = d.bf;
     } else {
-      const u32x4 rope = d.pc[4];
-      const uint32_t msk = d.valid ? 0xFFFFFFFFu : 0u;
-      *reinterpret_cast<u32x4*>(kt + drow * kKsRow + kDV * 2 + 16 * dcc) = rope & msk;
-      if (dcc == 0) bs[drow] = d.valid ? 0.0f : -INFINITY;
+      asm volatile("" : "+v"(d.bf));
     }
+  };
+  // the rope piece (held in pc[0]) and the score bias; an absent slot
+  // stores zeros and a -inf bias
+  auto deq_rope = [&](const Deq& d, uint8_t* kt, float* bs) {
+    const uint32_t msk = d.id >= 0 ? 0xFFFFFFFFu : 0u;
+    *reinterpret_cast<u32x4*>(kt + drow * kKsRow + kDV * 2 + 16 * dcc) = d.pc[0] & msk;
+    if (dcc == 0) bs[drow] = d.id >= 0 ? 0.0f : -INFINITY;
+  };
+  auto deq_full = [&](const uint8_t* stage, int step, uint8_t* kt, float* bs) __attribute__((always_inline)) {
+    Deq d;
+    deq_load(d, stage, step);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b > 0) deq_scale(d, b);
+      if (b < 3) deq_piece(d, b + 1);
+      deq_mask(d, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        deqA(d, 8 * b + i);
+        deqB(d, 8 * b + i);
+        deqC(d, kt, 8 * b + i);
+      }
+    }
+    deq_piece(d, 4);
+    deq_rope(d, kt, bs);
   };
 
   f32x16 o[kVTiles];
@@ -233,69 +292,116 @@ sparse_mla_h128_kernel(const Params p) {
   bool ovf;
 
   constexpr int kPf = 2;                     // fragment prefetch distance
-  constexpr int kRing = kPf + 2;
-  constexpr int kDeq0 = 8;                   // dequantisation: wait + scales, then 5 pieces
-  constexpr int kSm0 = 2;                    // softmax slices from this P.V group on
+  constexpr int kRing = kPf + 1;
 
-  // Softmax of one step's scores held in acc (lane: head c32, 16 slots),
-  // in slices: part 0 scales, biases and takes the maximum, parts 1..8 the
-  // weights (2 each), parts 9 and 10 pack P^T for slot chunks 0 and 1
-  // (lane (head c32, kg) holds slots 16ch + 4kg + {0..3, 8..11}).
-  float m_use = 0.0f;
-  auto softmax_part = [&](f32x16& acc, const float* bs, bf16x8 (&pn)[2], int part) {
-    if (part == 0) {
-      float lmx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 bi = *reinterpret_cast<const float4*>(bs + 8 * j + 4 * kg);
-        acc[4 * j] = fmaf(acc[4 * j], p.scale_log2, bi.x);
-        acc[4 * j + 1] = fmaf(acc[4 * j + 1], p.scale_log2, bi.y);
-        acc[4 * j + 2] = fmaf(acc[4 * j + 2], p.scale_log2, bi.z);
-        acc[4 * j + 3] = fmaf(acc[4 * j + 3], p.scale_log2, bi.w);
-        lmx = fmaxf(lmx, fmaxf(fmaxf(acc[4 * j], acc[4 * j + 1]),
-                               fmaxf(acc[4 * j + 2], acc[4 * j + 3])));
-      }
-      mall = fmaxf(mall, lmx);
-      const float hmx = fmaxf(lmx, __shfl_xor(lmx, 32));   // head c32 in both kg
-      m = m == -INFINITY ? hmx : m;                       // first step with a valid slot
-      ovf = ovf || lmx > m + kMaxExp;
-      m_use = m == -INFINITY ? 0.0f : m;
-    } else if (part <= 8) {
-      // a score beyond m + kMaxExp sets ovf and the row is run again, so
-      // its weight need not be finite
-#pragma unroll
-      for (int e = 2 * (part - 1); e < 2 * part; ++e) {
-        acc[e] = __builtin_amdgcn_exp2f(acc[e] - m_use);
-        l += acc[e];
-      }
+  // Softmax of one step's scores (lane: head c32, 16 slots e in acc), in
+  // stages that the loop skews over consecutive P.V MFMAs:
+  //   F(i): scores 2i, 2i + 1 scaled and biased; M(i): their maximum taken;
+  //   R: the head's maximum, the reference and the overflow check (after a
+  //     lane exchange);
+  //   S(e), X(e), L(e): score e minus the reference, its exponential, its
+  //     sum into l;
+  //   W(e) (e even): slots e, e + 1 of P^T packed (lane (head c32, kg) holds
+  //     slots 16ch + 4kg + {0..3, 8..11} of chunk ch = e / 8).
+  // The biases bia[j] (slots 8j + 4kg .. +3) are read beforehand.
+  float m_use = 0.0f, lmx = -INFINITY, hmx = -INFINITY;
+  float4 bia[4];
+  uint32_t pk[3];
+  auto bias_read = [&](const float* bs, int j) {
+    bia[j] = *reinterpret_cast<const float4*>(bs + 8 * j + 4 * kg);
+  };
+  auto smF = [&](f32x16& acc, int i) {
+    const int e = 2 * i;
+    const float4 bv = bia[e >> 2];
+    acc[e] = fmaf(acc[e], p.scale_log2, (e & 3) == 0 ? bv.x : bv.z);
+    acc[e + 1] = fmaf(acc[e + 1], p.scale_log2, (e & 3) == 0 ? bv.y : bv.w);
+    asm volatile("" : "+v"(acc[e]), "+v"(acc[e + 1]));
+  };
+  auto smM = [&](const f32x16& acc, int i) {
+    const float mx = fmaxf(acc[2 * i], acc[2 * i + 1]);
+    lmx = i == 0 ? mx : fmaxf(lmx, mx);
+    asm volatile("" : "+v"(lmx));
+  };
+  auto smR0 = [&]() {
+    mall = fmaxf(mall, lmx);
+    // head c32 in both kg: the two 32-lane halves exchanged by a VALU swap
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmx), __float_as_uint(lmx),
+                                                     false, false);
+    hmx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    asm volatile("" : "+v"(hmx));
+  };
+  auto smR1 = [&]() {
+    m = m == -INFINITY ? hmx : m;            // first step with a valid slot
+    ovf = ovf || lmx > m + kMaxExp;
+    m_use = m == -INFINITY ? 0.0f : m;
+    asm volatile("" : "+v"(m_use));
+  };
+  // a score beyond m + kMaxExp sets ovf and the row is run again, so its
+  // weight need not be finite
+  auto smS = [&](f32x16& acc, int e) {
+    acc[e] = acc[e] - m_use;
+    asm volatile("" : "+v"(acc[e]));
+  };
+  auto smX = [&](f32x16& acc, int e) {
+    acc[e] = __builtin_amdgcn_exp2f(acc[e]);
+    asm volatile("" : "+v"(acc[e]));
+  };
+  auto smL = [&](const f32x16& acc, int e) {
+    l += acc[e];
+    asm volatile("" : "+v"(l));
+  };
+  auto smW = [&](const f32x16& acc, bf16x8 (&pn)[2], int e) {
+    const int ch = e >> 3, wd = (e >> 1) & 3;
+    const uint32_t w = pack_bf16x2_hw(acc[e], acc[e + 1]);
+    if (wd < 3) {
+      pk[wd] = w;
+      asm volatile("" : "+v"(pk[wd]));
     } else {
-      const int ch = part - 9;
-      const uint4 u = make_uint4(pack_bf16x2_hw(acc[8 * ch], acc[8 * ch + 1]),
-                                 pack_bf16x2_hw(acc[8 * ch + 2], acc[8 * ch + 3]),
-                                 pack_bf16x2_hw(acc[8 * ch + 4], acc[8 * ch + 5]),
-                                 pack_bf16x2_hw(acc[8 * ch + 6], acc[8 * ch + 7]));
+      const uint4 u = make_uint4(pk[0], pk[1], pk[2], w);
       pn[ch] = *reinterpret_cast<const bf16x8*>(&u);
     }
   };
+  auto softmax_full = [&](f32x16& acc, const float* bs, bf16x8 (&pn)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bias_read(bs, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { smF(acc, i); smM(acc, i); }
+    smR0();
+    smR1();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      smS(acc, e);
+      smX(acc, e);
+      smL(acc, e);
+      if (e & 1) smW(acc, pn, e - 1);
+    }
+  };
 
-  // ---- iteration k, two phases of instruction groups (scheduling barriers
-  // between groups):
-  //   1. the 36 MFMAs of S^T(k) (two accumulator chains) from tile k, with
-  //      the loads of step k+2 (groups 0..5) and the dequantisation of step
-  //      k+1 into its tile (groups 8..13) between them;
-  //   2. the 32 MFMAs of O^T += V^T(k-1).P^T(k-1) from tile k-1 (tile q % 16,
-  //      slot chunk q / 16), with the softmax of step k into pn = P(k)
-  //      between them (groups 2..12).
-  // Fragments are read kPf MFMAs ahead into a ring of kPf + 2 kept live one
-  // MFMA longer; only one ring is live at a time.
-  auto iter = [&](int k, f32x16& acc, bf16x8 (&pa)[2], bf16x8 (&pn)[2],
-                  uint8_t* dma_stage, const uint8_t* deq_stage,
-                  const int32_t (&sid)[kDmaInsts], int32_t (&sid_next)[kDmaInsts]) {
+  // ---- iteration k: 68 instruction groups, one MFMA each (scheduling
+  // barriers between groups), the other work spread so that each group
+  // holds about as much VALU work as its MFMA covers:
+  //   phase 1, groups 0..35: the MFMAs of S^T(k) from tile k; the
+  //     dequantisation of step k+1 (its rows landed in raw buffer
+  //     (k+1) % 2) into tile k+1: stages A, B, C of half-word h in groups
+  //     3 + h, 4 + h, 5 + h (the last C in phase 2), raw piece b read in
+  //     group 8b, block scale b in group 8b + 1, the rope and bias in group
+  //     35; the row ids of step k+3 read;
+  //   phase 2, groups 0..31: the MFMAs of O^T += V^T(k-1).P^T(k-1) from tile
+  //     k-1 (tile q % 16, slot chunk q / 16); the loads of step k+3's rows
+  //     into the raw buffer just dequantised (groups 0, 1 and 27..30); the
+  //     softmax of step k into pn = P(k): biases read in groups 0, 1, F(i)
+  //     in group 3 + i, M(i) in 4 + i, R in 12 and 13, S(e), X(e), L(e) in
+  //     14 + e, 15 + e, 16 + e, W(e) in 17 + e.
+  // Fragments are read kPf MFMAs ahead into a ring of kPf + 1.
+  auto iter = [&](int k, f32x16& acc, bf16x8 (&pa)[2], bf16x8 (&pn)[2], uint8_t* raw) {
     const uint8_t* ktc = ks[k % 3];          // step k: scores
     const uint8_t* ktp = ks[(k + 2) % 3];    // step k-1: P.V
     uint8_t* ktn = ks[(k + 1) % 3];          // step k+1: dequantised now
     const float* bsc = bias[k % 3];
     float* bsn = bias[(k + 1) % 3];
+    int32_t idl;
+    int32_t sid[kDmaInsts];
+    Deq dq;
     {
       auto kfrag = [&](int i) {
         return *reinterpret_cast<const bf16x8*>(ktc + c32 * kKsRow + (16 * i + 8 * kg) * 2);
@@ -303,35 +409,32 @@ sparse_mla_h128_kernel(const Params p) {
       bf16x8 fr[kRing];
 #pragma unroll
       for (int i = 0; i < kPf; ++i) fr[i] = kfrag(i);
-      // two accumulator chains (even and odd contraction steps): a chain of
-      // dependent MFMAs issues at half rate
-      f32x16 acc2;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { acc[e] = 0.0f; acc2[e] = 0.0f; }
-      Deq dq;
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
 #pragma unroll
       for (int g = 0; g < kQSteps; ++g) {
         if (g + kPf < kQSteps) fr[(g + kPf) % kRing] = kfrag(g + kPf);
-        if (g > 0) asm volatile("" ::"v"(fr[(g - 1) % kRing]));
         __builtin_amdgcn_sched_barrier(0);
-        if (g % 2 == 0)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[g % kRing], qb[g], acc, 0, 0, 0);
-        else
-          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[g % kRing], qb[g], acc2, 0, 0, 0);
-        // loads of step k+2
-        if (g < kDmaInsts) dma_row_id(dma_stage, sid[g], g);
-        // dequantisation of step k+1 (its loads were issued one iteration ago)
-        if (g == kDeq0) {
-          wait_vm_dma();
-          deq_load(dq, deq_stage, k + 1);
-        } else if (g > kDeq0 && g <= kDeq0 + 5) {
-          if (g - kDeq0 < 5) deq_fetch(dq, g - kDeq0);
-          deq_store(dq, ktn, bsn, g - kDeq0 - 1);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[g % kRing], qb[g], acc, 0, 0, 0);
+        if (g == 0) {
+          wait_vm_dma();   // the rows of step k+1
+          deq_load(dq, raw, k + 1);
+        } else if (g == 1) {
+          // lane j < 8 reads the id of row j of step k+3
+          idl = ids[(k + 3) * kStep + wave * kW128Slots + (lane & 7)];
+        } else if (g == 5 || g == 6) {
+#pragma unroll
+          for (int j = 4 * (g - 5); j < 4 * (g - 4); ++j) sid[j] = __builtin_amdgcn_readlane(idl, j);
         }
+        if (g % 8 == 0 && g > 0 && g <= 32) deq_piece(dq, g / 8);
+        if (g % 8 == 1 && g > 1 && g <= 25) deq_scale(dq, g / 8);
+        if (g % 8 == 3 && g <= 27) deq_mask(dq, g / 8);
+        if (g >= 5) deqC(dq, ktn, g - 5);
+        if (g >= 4) deqB(dq, g - 4);
+        if (g >= 3 && g < 35) deqA(dq, g - 3);
+        if (g == kQSteps - 1) deq_rope(dq, ktn, bsn);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] += acc2[e];
     }
     {
       const uint8_t* vbase = ktp + (4 * kg + (sl >> 2)) * kKsRow + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
@@ -348,19 +451,35 @@ sparse_mla_h128_kernel(const Params p) {
 #pragma unroll
       for (int q = 0; q < 2 * kVTiles; ++q) {
         if (q + kPf < 2 * kVTiles) vf[(q + kPf) % kRing] = vfrag(q + kPf);
-        if (q > 0) asm volatile("" ::"v"(vf[(q - 1) % kRing]));
         __builtin_amdgcn_sched_barrier(0);
         // inline asm: the AGPR form of the MFMA for O^T (the 256 AGPRs) while
         // the score MFMAs above use the VGPR form; P (pa) was written by VALU
         // at least one phase earlier, so no wait states are owed here
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                      : "+a"(o[q & 15]) : "v"(vf[q % kRing]), "v"(pa[q >> 4]));
-        // softmax of step k (its scores were summed after phase 1)
-        if (q >= kSm0 && q < kSm0 + 11) softmax_part(acc, bsc, pn, q - kSm0);
+        if (q == 0) deqC(dq, ktn, 31);
+        // loads of step k+3 into the raw buffer whose rows were dequantised
+        // in phase 1 (every read of it has been waited for)
+        if (q < 2) {
+          dma_row_id(raw, sid[2 * q], 2 * q);
+          dma_row_id(raw, sid[2 * q + 1], 2 * q + 1);
+          bias_read(bsc, 2 * q);
+          bias_read(bsc, 2 * q + 1);
+        } else if (q >= 27 && q < 31) {
+          dma_row_id(raw, sid[q - 23], q - 23);
+        }
+        // softmax of step k
+        if (q >= 4 && q < 12) smM(acc, q - 4);
+        if (q >= 3 && q < 11) smF(acc, q - 3);
+        if (q == 12) smR0();
+        if (q == 13) smR1();
+        if (q >= 17 && (q - 17) % 2 == 0) smW(acc, pn, q - 17);
+        if (q >= 16) smL(acc, q - 16);
+        if (q >= 15 && q < 31) smX(acc, q - 15);
+        if (q >= 14 && q < 30) smS(acc, q - 14);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    read_ids(sid_next, k + 3);   // ids of the next iteration's row loads
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
   };
@@ -375,7 +494,7 @@ sparse_mla_h128_kernel(const Params p) {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qb[i], acc, 0, 0, 0);
     }
   };
-  auto run_pass = [&]() {
+  auto run_pass = [&](bool first) {
 #pragma unroll
     for (int d = 0; d < kVTiles; ++d) {
 #pragma unroll
@@ -389,47 +508,35 @@ sparse_mla_h128_kernel(const Params p) {
       uint8_t* r0 = RawBuf<0>::get();
       uint8_t* r1 = RawBuf<1>::get();
       // prologue: rows of steps 0 and 1 in flight, step 0 dequantised into
-      // tile 0, its scores and P taken, step 1 dequantised into tile 1
+      // tile 0, the rows of step 2 requested, the scores and P of step 0
+      // taken, step 1 dequantised into tile 1, the rows of step 3 requested
       dma(r0, 0);
       dma(r1, 1);
-      {
-        Deq d0;
+      if (first) {
+        load_q();
+        wait_vm_dma_q();
+      } else {
         wait_vm_dma();
-        deq_load(d0, r0, 0);
-#pragma unroll
-        for (int b = 0; b < 5; ++b) {
-          if (b < 4) deq_fetch(d0, b + 1);
-          deq_store(d0, ks[0], bias[0], b);
-        }
       }
+      deq_full(r0, 0, ks[0], bias[0]);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       dma(r0, 2);   // raw buffer 0 (step 0) was read by this wave only
       qk0(acc);
-#pragma unroll
-      for (int part = 0; part < 11; ++part) softmax_part(acc, bias[0], pA, part);
-      {
-        Deq d1;
-        wait_vm_dma();
-        deq_load(d1, r1, 1);
-#pragma unroll
-        for (int b = 0; b < 5; ++b) {
-          if (b < 4) deq_fetch(d1, b + 1);
-          deq_store(d1, ks[1], bias[1], b);
-        }
-      }
-      int32_t idA[kDmaInsts], idB[kDmaInsts];
-      read_ids(idA, 3);
+      softmax_full(acc, bias[0], pA);
+      wait_vm_dma();
+      deq_full(r1, 1, ks[1], bias[1]);
+      dma(r1, 3);   // raw buffer 1 (step 1) was read by this wave only
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
-      // iteration k: scores of step k, P.V of step k-1, loads of k+2,
-      // dequantisation of k+1; steps past nsteps are empty (every bias
-      // -inf, P zero)
+      // iteration k: scores of step k, P.V of step k-1, dequantisation of
+      // k+1 from raw buffer (k+1) % 2, then the loads of k+3 into it; steps
+      // past nsteps are empty (every bias -inf, P zero)
       // (iteration nsteps does the P.V of the last step; its own scores are
       // those of an empty step)
       for (int k = 1; k <= nsteps; k += 2) {
-        iter(k, acc, pA, pB, r1, r0, idA, idB);   // loads of k+2 into raw 1, step k+1 from raw 0
-        if (k + 1 <= nsteps) iter(k + 1, acc, pB, pA, r0, r1, idB, idA);
+        iter(k, acc, pA, pB, r0);
+        if (k + 1 <= nsteps) iter(k + 1, acc, pB, pA, r1);
       }
     }
   };
@@ -441,7 +548,7 @@ sparse_mla_h128_kernel(const Params p) {
   m = -INFINITY;
   mall = -INFINITY;
   ovf = false;
-  run_pass();
+  run_pass(true);
   mfma_drain();
   // a score beyond the clamp anywhere in the block: run again with the true
   // maximum as reference
@@ -454,7 +561,7 @@ sparse_mla_h128_kernel(const Params p) {
     ovf = false;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads of the first pass
     __syncthreads();
-    run_pass();
+    run_pass(false);
     mfma_drain();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // trailing loads into LDS
