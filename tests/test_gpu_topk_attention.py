@@ -318,7 +318,10 @@ def test_sparse_mla_score_jump_reruns_exactly(H, T):
 
 @pytest.mark.parametrize("T,topk", [(5, 2048), (3, 100), (128, 160), (64, 2048),
                                     # more than 128 rows: one 128-head block per row
-                                    (129, 2048), (200, 300), (256, 256), (300, 64)])
+                                    (129, 2048), (200, 300), (256, 256), (300, 64),
+                                    # one and two 32-slot steps per block (the
+                                    # prologue alone, one loop iteration)
+                                    (160, 24), (140, 40)])
 def test_sparse_mla_128_heads_fp8_edges_and_determinism(T, topk):
     """128 heads over an fp8 cache, the 128-head kernel: up to 128 rows
     split over KV (2 splits at 128 rows, 4 at 64, 16 at 5; merged from bf16
