@@ -57,7 +57,7 @@ constexpr int kRawStage = 4 * kRawWave;                     // 20992
 constexpr int kRowPieces = kRawRow / 16;                    // 41 16-byte pieces per row
 constexpr int kDmaInsts = kW128Slots;                       // one load instruction per row
 constexpr int kIds128 = kMaxSplit + 4 * kStep;              // ids of a row + overrun
-static_assert(kDmaInsts == 8, "row ids are read as two int4");
+static_assert(kDmaInsts == 8, "a step's row ids are read by lanes 0..7 of the wave");
 constexpr int kQSteps = kDQK / 16;                          // 36 contraction steps
 constexpr int kVTiles = kDV / 32;                           // 16 value tiles
 // output staging: 16 rows of 1024 bytes per wave; the 1040-byte stride puts
@@ -84,20 +84,13 @@ struct RawBuf<1> { static __device__ __forceinline__ uint8_t* get() { return g_r
 // raw buffer is read only after wait_vm_dma, which (the asm has a memory
 // clobber) the compiler does not move reads above, and every wave waits
 // for all of its loads before the LDS is used otherwise or the wave ends.
-__device__ __forceinline__ void lds_dma16(const uint8_t* src, uint32_t lds_addr) {
-  // M0 = the wave's LDS destination (the operand is bound to M0, so the
-  // compiler writes it); lane i writes 16 bytes at M0 + 16 i. One wait state
-  // between the write of M0 and the load that reads it.
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "{m0}"(lds_addr)
-               : "memory");
-}
-
-// The same load of one 656-byte row, lanes 0..40, with the other lanes
+// One load instruction brings one 656-byte row: M0 = the row's LDS
+// destination (the operand is bound to M0, so the compiler writes it), lane
+// i < 41 writes bytes [16i, 16i+16) at M0 + 16 i; the other lanes are
 // switched off inside the asm (EXEC saved and restored there), so that the
 // code around it stays one basic block: the compiler does not move work
 // between basic blocks of the unrolled loop as it would around a branch.
+// One wait state between the write of M0 and the load that reads it.
 constexpr uint64_t kRowLanes = (1ull << kRowPieces) - 1;
 __device__ __forceinline__ void lds_dma_row(const uint8_t* src, uint32_t lds_addr) {
   uint64_t saved;
