@@ -244,6 +244,9 @@ def main():
     slots = torch.empty(T, w.topk, dtype=i32, device=dev)
     # top-k histogram counted by the indexer; the top-k clears it after use
     key_hist = nsa.new_key_hist(T, dev) if idt == nsa.DTYPE_FP8_E4M3 else None
+    # bitmaps of the top-k whose long rows are spread over many blocks
+    tk_ws = torch.empty(max(nsa.topk_hist_workspace_size(T, w.max_seqlen_k, w.topk), 16),
+                        dtype=torch.uint8, device=dev)
     out = torch.empty(T, w.heads, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(T, w.heads, dtype=torch.float32, device=dev)
     ws = torch.empty(max(nsa.sparse_mla_workspace_size(T, w.heads, w.topk), 16),
@@ -273,7 +276,7 @@ def main():
         nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                w.max_seqlen_k, table=md["real_page_table"],
                                token_to_req=md["token_to_req"], out=slots,
-                               key_hist=key_hist)
+                               key_hist=key_hist, workspace=tk_ws)
         if e: e[3].record()
         attn(w.q, cache, kvd, slots, w.sm_scale, md["nsa_cache_seqlens"],
              out=out, lse=lse, workspace=ws)

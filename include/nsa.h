@@ -272,12 +272,22 @@ int nsa_topk_transform(const float* logits, int64_t logits_stride,
  * Every choice gives bit-identical logits and counts.
  *
  * nsa_topk_transform_hist: as nsa_topk_transform, with key_hist from
- * nsa_indexer_logits_hist over the same logits (16-byte aligned); it needs
- * no workspace. It sets rows 0..T-1 of key_hist back to zero, so one buffer
- * serves every layer. A row whose counts do not add up to its length takes
- * a slower exact path; any other mismatch between key_hist and the logits is
- * the caller's contract (the result is then unspecified but stays in the
- * bounds of `out`).
+ * nsa_indexer_logits_hist over the same logits (16-byte aligned). It sets
+ * rows 0..T-1 of key_hist back to zero, so one buffer serves every layer. A
+ * row whose counts do not add up to its length takes a slower exact path;
+ * any other mismatch between key_hist and the logits is the caller's
+ * contract (the result is then unspecified but stays in the bounds of `out`).
+ *   workspace   optional device scratch of nsa_topk_hist_workspace_size()
+ *               bytes, 16-byte aligned, owned by the caller, contents
+ *               irrelevant on entry (ws_bytes is its size; smaller is
+ *               NSA_ERR_WORKSPACE). With it, a batch of at most 128
+ *               rows longer than 16384 positions has its rows classified by
+ *               blocks of 16384 positions spread over the whole GPU instead
+ *               of one block per row (a second launch then finishes each
+ *               row). NULL, or a size of 0 from the query, runs one block
+ *               per row. Results are identical either way.
+ * nsa_topk_hist_workspace_size: that size for T rows (0 when the split is
+ * not used: T > 128, max_seqlen_k <= max(topk, 16384) or > 262144).
  */
 int nsa_indexer_logits_hist(const void* q, int q_dtype, const float* weights,
                             const void* k_index_cache, int k_dtype,
@@ -288,12 +298,15 @@ int nsa_indexer_logits_hist(const void* q, int q_dtype, const float* weights,
                             float* logits, int64_t logits_stride,
                             uint32_t* key_hist, int rows_per_request,
                             void* stream);
+int nsa_topk_hist_workspace_size(int T, int max_seqlen_k, int topk,
+                                 size_t* bytes);
 int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
                             const int32_t* lengths, int T, int topk,
                             int max_seqlen_k, const int32_t* table,
                             int64_t table_stride, int64_t table_rows, const int32_t* token_to_req,
                             int page_size, uint32_t* key_hist, int32_t* out,
-                            int64_t out_stride, void* stream);
+                            int64_t out_stride, void* workspace, size_t ws_bytes,
+                            void* stream);
 
 /* ---- a3: page-table transform ---------------------------------------------------
  * [nsa-fork] forward_decode / forward_extend:

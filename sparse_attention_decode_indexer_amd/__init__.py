@@ -188,12 +188,24 @@ def nsa_indexer_logits(q, weights, index_cache, real_page_table, token_to_req,
     return logits
 
 
+def topk_hist_workspace_size(T, max_seqlen_k, topk):
+    """Bytes of the optional workspace of the top-k with key_hist (0: unused)."""
+    ws = ctypes.c_size_t(0)
+    call("nsa_topk_hist_workspace_size", int(T), int(max_seqlen_k), int(topk),
+         ctypes.byref(ws))
+    return ws.value
+
+
 def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
-                       token_to_req=None, out=None, key_hist=None):
+                       token_to_req=None, out=None, key_hist=None,
+                       workspace=None, split=True):
     """Top-k positions per row (ascending position order, -1 padded), or
     physical slots when ``table`` (the compact page table) is given. With
     ``key_hist`` (filled by nsa_indexer_logits on the same logits) the logits
-    are read once and key_hist is cleared for reuse."""
+    are read once and key_hist is cleared for reuse; long rows are then
+    split over many blocks through ``workspace`` (uint8, at least
+    topk_hist_workspace_size bytes; allocated here when not given), unless
+    ``split`` is False."""
     _check(lengths, "lengths", torch.int32, 1)
     T = lengths.numel()
     if logits is not None:
@@ -217,11 +229,19 @@ def nsa_topk_transform(logits, lengths, topk, max_seqlen_k, table=None,
         _check(key_hist, "key_hist", torch.int32, 2)
         if key_hist.shape[0] < T or key_hist.shape[1] != KEY_BINS:
             raise ValueError("key_hist must be [>= T, 4096]")
+        need = topk_hist_workspace_size(T, max_seqlen_k, topk) if split else 0
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=lengths.device)
+        if not need:
+            workspace = None
+        if workspace is not None:
+            _check(workspace, "workspace", torch.uint8, 1)
         call("nsa_topk_transform_hist", _ptr(logits),
              logits.stride(0) if logits is not None else 0, _ptr(lengths), T, topk,
              max_seqlen_k, _ptr(table), table.stride(0) if table is not None else 0,
              trows, _ptr(token_to_req), PAGE_SIZE, _ptr(key_hist), _ptr(out),
-             out.stride(0), _stream())
+             out.stride(0), _ptr(workspace),
+             workspace.numel() if workspace is not None else 0, _stream())
         return out
     ws = ctypes.c_size_t(0)
     call("nsa_topk_workspace_size", T, max_seqlen_k, topk, ctypes.byref(ws))

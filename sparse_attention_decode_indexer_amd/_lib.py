@@ -26,8 +26,11 @@ SIGNATURES = {
         P, c_int, P, P, c_int, c_i64, P, c_i64, c_i64, P, P, c_int, c_int, c_int,
         c_int, c_int, P, c_i64, P, c_int, P]),
     "nsa_topk_workspace_size": (c_int, [c_int, c_int, c_int, ctypes.POINTER(c_size)]),
+    "nsa_topk_hist_workspace_size": (c_int, [c_int, c_int, c_int,
+                                             ctypes.POINTER(c_size)]),
     "nsa_topk_transform_hist": (c_int, [
-        P, c_i64, P, c_int, c_int, c_int, P, c_i64, c_i64, P, c_int, P, P, c_i64, P]),
+        P, c_i64, P, c_int, c_int, c_int, P, c_i64, c_i64, P, c_int, P, P, c_i64, P,
+        c_size, P]),
     "nsa_topk_transform": (c_int, [
         P, c_i64, P, c_int, c_int, c_int, P, c_i64, c_i64, P, c_int, P, c_i64, P,
         c_size, P]),

@@ -48,9 +48,12 @@ __device__ __forceinline__ void for_each_key(const float* row, int n, bool vec,
   }
 }
 
-// Exclusive block-wide prefix sum of v; *total receives the sum.
+// Exclusive prefix sum of v over a block of NT threads; *total receives the
+// sum. wave_tot holds 2 * NT / 64 + 1 ints.
+template <int NT = kThreads>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot,
                                                     int* total) {
+  constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -121,22 +124,23 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, int nb,
 template <int NB>
 __device__ __forceinline__ void publish_threshold(const uint32_t (&c)[NB], uint32_t above,
                                                   int krem, uint32_t* s_sel) {
-  uint32_t own = 0;
+  // walk the bins from the top with selects only (no early exit, so the
+  // counts stay in registers)
+  uint32_t a = above, sel_a = 0, sel_c = 0;
+  int sel_i = -1;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) own += c[i];
-  if (above < (uint32_t)krem && above + own >= (uint32_t)krem) {
-    uint32_t a = above;
-#pragma unroll
-    for (int i = NB - 1; i >= 0; --i) {
-      if (a + c[i] >= (uint32_t)krem) {
-        s_sel[0] = NB * threadIdx.x + i;
-        s_sel[1] = krem - a;
-        s_sel[2] = (a + c[i] == (uint32_t)krem) ? 1u : 0u;
-        s_sel[3] = c[i];
-        break;
-      }
-      a += c[i];
-    }
+  for (int i = NB - 1; i >= 0; --i) {
+    const bool hit = sel_i < 0 && a + c[i] >= (uint32_t)krem;
+    sel_i = hit ? i : sel_i;
+    sel_a = hit ? a : sel_a;
+    sel_c = hit ? c[i] : sel_c;
+    a += c[i];
+  }
+  if (above < (uint32_t)krem && a >= (uint32_t)krem) {
+    s_sel[0] = NB * threadIdx.x + sel_i;
+    s_sel[1] = krem - sel_a;
+    s_sel[2] = (sel_a + sel_c == (uint32_t)krem) ? 1u : 0u;
+    s_sel[3] = sel_c;
   }
 }
 
@@ -307,6 +311,122 @@ topk_hist_kernel(const float* __restrict__ logits, int64_t logits_stride,
     const uint32_t lo = sub[0][b] + sub[1][b] + sub[2][b] + sub[3][b];
     const uint32_t hi = sub[0][b + 1] + sub[1][b + 1] + sub[2][b + 1] + sub[3][b + 1];
     dst[b2] = lo | (hi << 16);
+  }
+}
+
+// The exact selection once the keys of a row are classified against the
+// threshold bin `bin` (the bin holding the topk-th largest key, krem of its
+// keys still to keep; `exact`: the whole bin is kept): the LDS `bitmap` holds
+// the positions of the keys above the bin, cand_pos[0, nc) those of the keys
+// inside it, in any order. Two 10-bit radix passes over the candidates' keys
+// find the exact threshold, ties on it keep the lowest positions (a radix
+// select on position), the kept candidates are marked too, and a block-wide
+// scan of the bitmap writes the kept positions in ascending order (through
+// the page-table row trow when given). Every thread of the block calls it.
+template <int kCP>
+__device__ __forceinline__ void finish_select(
+    const float* row, int n, int topk, uint32_t bin, int krem, bool exact, int nc,
+    const int32_t* trow, const int32_t* lengths, uint32_t* hist, uint32_t* bitmap,
+    uint32_t* cand_key, int32_t* cand_pos, int* scan_buf, uint32_t* s_sel,
+    int32_t* orow) {
+  const int tid = threadIdx.x;
+  const int nw = (n + 31) >> 5;
+  // keys of the candidates, read back from the row (recently read, so
+  // mostly cache hits)
+  for (int i = tid; i < nc; i += kThreads) cand_key[i] = order_key(row[cand_pos[i]]);
+  // the row's page-table entries for the output, loaded now (branch-free:
+  // without a table the loads read lengths[0]) and put in LDS once the
+  // candidates are no longer needed
+  constexpr int kTabPer = kMapBits / NSA_PAGE_SIZE / kThreads;
+  int32_t tab[kTabPer];
+  {
+    const int32_t* tsrc = trow ? trow : lengths;
+    const int lim = trow ? ((n + NSA_PAGE_SIZE - 1) >> 6) - 1 : 0;
+#pragma unroll
+    for (int k = 0; k < kTabPer; ++k) tab[k] = tsrc[min(tid + k * kThreads, lim)];
+  }
+
+  // ---- exact threshold among the candidates (bits 19..10, then 9..0)
+  uint32_t prefix = bin << 20, pmask = 0xFFF00000u;
+  for (int pass = 0; pass < 2 && !exact; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    hist[tid] = 0;   // 1024 bins
+    __syncthreads();
+    for (int i = tid; i < nc; i += kThreads) {
+      const uint32_t k = cand_key[i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    {
+      const uint32_t c1[1] = {hist[tid]};
+      int tot1;
+      const int ex1 = block_exclusive_scan((int)c1[0], scan_buf, &tot1);
+      publish_threshold<1>(c1, (uint32_t)(tot1 - ex1) - c1[0], krem, s_sel);
+    }
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    pmask |= 1023u << shift;
+    krem = (int)s_sel[1];
+    exact = s_sel[2] != 0;
+    __syncthreads();
+  }
+  // ---- equal full keys at the threshold: keep the krem lowest positions,
+  // a radix select on tk = kMapBits - 1 - position (unique, so exact)
+  uint32_t tprefix = 0, tmask = 0;
+  for (int pass = 0; pass < 2 && !exact; ++pass) {
+    const int shift = pass == 0 ? 9 : 0;
+    if (tid < kTieBins) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < nc; i += kThreads) {
+      const uint32_t tk = (uint32_t)(kMapBits - 1 - cand_pos[i]);
+      if (cand_key[i] == prefix && (tk & tmask) == tprefix)
+        atomicAdd(&hist[(tk >> shift) & (kTieBins - 1)], 1u);
+    }
+    __syncthreads();
+    {
+      const uint32_t c1[1] = {tid < kTieBins ? hist[tid] : 0u};
+      int tot1;
+      const int ex1 = block_exclusive_scan((int)c1[0], scan_buf, &tot1);
+      publish_threshold<1>(c1, (uint32_t)(tot1 - ex1) - c1[0], krem, s_sel);
+    }
+    __syncthreads();
+    tprefix |= s_sel[0] << shift;
+    tmask |= (uint32_t)(kTieBins - 1) << shift;
+    krem = (int)s_sel[1];
+    __syncthreads();
+  }
+  for (int i = tid; i < nc; i += kThreads) {
+    const uint32_t mk = cand_key[i] & pmask;
+    const int pos = cand_pos[i];
+    const bool keep = mk > prefix ||
+        (mk == prefix && (exact || (uint32_t)(kMapBits - 1 - pos) >= tprefix));
+    if (keep) atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
+  }
+  __syncthreads();
+  int32_t* ptab = reinterpret_cast<int32_t*>(cand_key);   // >= 4096 entries
+  static_assert(kCP >= kTabPer * kThreads, "page table fits the candidate store");
+  if (trow) {
+#pragma unroll
+    for (int k = 0; k < kTabPer; ++k) ptab[tid + k * kThreads] = tab[k];
+  }
+
+  // ---- kept positions in ascending order: each thread owns a run of words
+  // (the scan's barriers also publish the page table)
+  const int per = (nw + kThreads - 1) / kThreads;
+  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
+  int kept;
+  int o = block_exclusive_scan(cnt, scan_buf, &kept);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = bitmap[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int i = w * 32 + b;
+      if (o < topk) orow[o] = trow ? (ptab[i >> 6] << 6) + (i & 63) : i;
+      ++o;
+    }
   }
 }
 
@@ -521,103 +641,241 @@ topk_select_kernel(const float* __restrict__ logits, int64_t logits_stride,
     }
   }
   __syncthreads();
-  const int nc = min(s_ncand, kCP);
-  // keys of the candidates, read back from the row (just read, so cached)
-  for (int i = tid; i < nc; i += kThreads) cand_key[i] = order_key(row[cand_pos[i]]);
-  // the row's page-table entries for the output, loaded now (branch-free:
-  // without a table the loads read lengths[0]) and put in LDS once the
-  // candidates are no longer needed
-  constexpr int kTabPer = kMapBits / NSA_PAGE_SIZE / kThreads;
-  int32_t tab[kTabPer];
-  {
-    const int32_t* tsrc = trow ? trow : lengths;
-    const int lim = trow ? ((n + NSA_PAGE_SIZE - 1) >> 6) - 1 : 0;
-#pragma unroll
-    for (int k = 0; k < kTabPer; ++k) tab[k] = tsrc[min(tid + k * kThreads, lim)];
-  }
+  finish_select<kCP>(row, n, topk, bin, krem, exact, min(s_ncand, kCP), trow,
+                     lengths, hist, bitmap, cand_key, cand_pos, scan_buf, s_sel,
+                     orow);
+}
 
-  // ---- exact threshold among the candidates (bits 19..10, then 9..0)
-  uint32_t prefix = bin << 20, pmask = 0xFFF00000u;
-  for (int pass = 0; pass < 2 && !exact; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    hist[tid] = 0;   // 1024 bins
-    __syncthreads();
-    for (int i = tid; i < nc; i += kThreads) {
-      const uint32_t k = cand_key[i];
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1u);
+
+// ---- split select (key_hist given, a workspace, rows longer than one
+// segment). One block per row reads at most ~20-25 GB/s, so a long row's pass
+// over its logits bounds the one-kernel select; here that pass is spread over
+// blocks of kSeg positions (topk_mark_kernel), which classify their keys
+// against the row's threshold bin into two bitmaps in the workspace, and one
+// block per row then finishes the exact selection from those bitmaps
+// (topk_finish_kernel), as the one-kernel select does after its pass.
+// Workspace row t (ws_row uint32 words, 16-byte aligned):
+//   [0, 4)                    {take the multi-pass select, bin, krem, exact},
+//                             written by the row's first segment block
+//   [kSplitParams, +mw)       bit p: the key of position p lies above the bin
+//   [kSplitParams + mw, +mw)  bit p: the key of position p lies in the bin
+// with mw = ceil(max_seqlen_k / 32) rounded up to a multiple of 4. Words of
+// positions at or past the row's length are never written; nothing has to be
+// zero on entry.
+constexpr int kSeg = 16384;                     // positions per mark block
+constexpr int kSegThreads = 256;
+constexpr int kSegVec = kSeg / (kSegThreads * 4);   // float4 per thread
+constexpr int kSplitParams = 16;
+
+__host__ __device__ constexpr int split_map_words(int max_seqlen_k) {
+  return ((max_seqlen_k + 31) / 32 + 3) & ~3;
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kSegThreads)
+topk_mark_kernel(const float* __restrict__ logits, int64_t logits_stride,
+                 const int32_t* __restrict__ lengths, int64_t rows, int topk,
+                 int max_seqlen_k, int segs,
+                 const uint32_t* __restrict__ key_hist,
+                 uint32_t* __restrict__ ws, int64_t ws_row, int mw) {
+  __shared__ int scan_buf[2 * (kSegThreads / 64) + 1];
+  __shared__ uint32_t s_sel[4];
+  // work groups are dealt to the 8 XCDs in turn (block b to XCD b % 8): the
+  // segments of row t all run on XCD t % 8, so each XCD's L2 fetches a row's
+  // histogram once for all of its segments (the grid covers T rounded up to
+  // a multiple of 8 rows)
+  const int xcd = blockIdx.x & 7;
+  const int j = blockIdx.x >> 3;
+  const int64_t t = 8 * (int64_t)(j / segs) + xcd;
+  const int seg0 = (j % segs) * kSeg;
+  const int tid = threadIdx.x;
+  if (t >= rows) return;
+  int n = lengths[t];
+  n = n < 0 ? 0 : (n > max_seqlen_k ? max_seqlen_k : n);
+  if (n <= topk || seg0 >= n) return;   // the finish kernel keeps 0..n-1
+  const float* row = logits + t * logits_stride;
+
+  // the whole segment is loaded before the threshold is known (clamped
+  // branch-free loads, as in the one-kernel select; VEC: positions
+  // [vend, n) are fixed up below)
+  const int vend = VEC ? (n & ~3) : n;
+  const int vlast = vend >= 4 ? vend - 4 : 0;
+  float v[kSegVec][4];
+#pragma unroll
+  for (int k = 0; k < kSegVec; ++k)
+    load4<VEC>(row, seg0 + k * (kSegThreads * 4) + tid * 4, vlast, n, v[k]);
+
+  // threshold bin from the row histogram: thread tid owns bins 16 tid ..
+  // 16 tid + 15
+  uint32_t c[16];
+  {
+    const uint4* h4 = reinterpret_cast<const uint4*>(key_hist + t * kKeyBins) + tid * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 x = h4[i];
+      c[4 * i] = x.x; c[4 * i + 1] = x.y; c[4 * i + 2] = x.z; c[4 * i + 3] = x.w;
     }
-    __syncthreads();
-    {
-      const uint32_t c1[1] = {hist[tid]};
-      int tot1;
-      const int ex1 = block_exclusive_scan((int)c1[0], scan_buf, &tot1);
-      publish_threshold<1>(c1, (uint32_t)(tot1 - ex1) - c1[0], krem, s_sel);
-    }
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    pmask |= 1023u << shift;
-    krem = (int)s_sel[1];
-    exact = s_sel[2] != 0;
-    __syncthreads();
   }
-  // ---- equal full keys at the threshold: keep the krem lowest positions,
-  // a radix select on tk = kMapBits - 1 - position (unique, so exact)
-  uint32_t tprefix = 0, tmask = 0;
-  for (int pass = 0; pass < 2 && !exact; ++pass) {
-    const int shift = pass == 0 ? 9 : 0;
-    if (tid < kTieBins) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < nc; i += kThreads) {
-      const uint32_t tk = (uint32_t)(kMapBits - 1 - cand_pos[i]);
-      if (cand_key[i] == prefix && (tk & tmask) == tprefix)
-        atomicAdd(&hist[(tk >> shift) & (kTieBins - 1)], 1u);
-    }
-    __syncthreads();
-    {
-      const uint32_t c1[1] = {tid < kTieBins ? hist[tid] : 0u};
-      int tot1;
-      const int ex1 = block_exclusive_scan((int)c1[0], scan_buf, &tot1);
-      publish_threshold<1>(c1, (uint32_t)(tot1 - ex1) - c1[0], krem, s_sel);
-    }
-    __syncthreads();
-    tprefix |= s_sel[0] << shift;
-    tmask |= (uint32_t)(kTieBins - 1) << shift;
-    krem = (int)s_sel[1];
-    __syncthreads();
+  uint32_t hs = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) hs += c[i];
+  int tot;
+  const int hex = block_exclusive_scan<kSegThreads>((int)hs, scan_buf, &tot);
+  uint32_t* prow = ws + t * ws_row;
+  if (tot != n) {   // not the histogram of these logits: multi-pass select
+    if (seg0 == 0 && tid == 0)
+      *reinterpret_cast<uint4*>(prow) = make_uint4(1u, 0u, 0u, 0u);
+    return;
   }
-  for (int i = tid; i < nc; i += kThreads) {
-    const uint32_t mk = cand_key[i] & pmask;
-    const int pos = cand_pos[i];
-    const bool keep = mk > prefix ||
-        (mk == prefix && (exact || (uint32_t)(kMapBits - 1 - pos) >= tprefix));
-    if (keep) atomicOr(&bitmap[pos >> 5], 1u << (pos & 31));
+  publish_threshold<16>(c, (uint32_t)(tot - hex) - hs, topk, s_sel);
+  __syncthreads();
+  const uint32_t bin = s_sel[0];
+  const bool multipass = s_sel[3] > (uint32_t)kCap || n > kMapBits;
+  if (seg0 == 0 && tid == 0)
+    *reinterpret_cast<uint4*>(prow) =
+        make_uint4(multipass ? 1u : 0u, bin, s_sel[1], s_sel[2]);
+  if (multipass) return;
+
+  if (VEC && vend < n) {   // the 1..3 positions past the last whole vector
+#pragma unroll
+    for (int k = 0; k < kSegVec; ++k) {
+      const int pos = seg0 + k * (kSegThreads * 4) + tid * 4;
+      if (pos == vend) {
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+          if (vend + e < n) v[k][e] = row[vend + e];
+      }
+    }
+  }
+  // the 8 lanes sharing a 32-bit word OR their nibbles in registers and one
+  // of them stores the word of each bitmap
+  uint32_t* amap = prow + kSplitParams;
+  uint32_t* bmap = amap + mw;
+  const int nw = (n + 31) >> 5;
+#pragma unroll
+  for (int k = 0; k < kSegVec; ++k) {
+    const int pos = seg0 + k * (kSegThreads * 4) + tid * 4;
+    uint32_t ma = 0, mb = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = pos + e < n;
+      const uint32_t kb = order_key(v[k][e]) >> 20;
+      ma |= (in && kb > bin) ? (1u << e) : 0u;
+      mb |= (in && kb == bin) ? (1u << e) : 0u;
+    }
+    const uint32_t wa = or_lanes8(ma << ((tid & 7) * 4));
+    const uint32_t wb = or_lanes8(mb << ((tid & 7) * 4));
+    const int word = pos >> 5;
+    if ((tid & 7) == 0 && word < nw) {
+      amap[word] = wa;
+      bmap[word] = wb;
+    }
+  }
+}
+
+// One 1024-thread block per row after topk_mark_kernel: clears the row of
+// key_hist, takes the threshold bin from the workspace, loads the above-bin
+// bitmap into LDS and lists the in-bin positions (ascending) as candidates,
+// then runs the same exact selection and ordered write as the one-kernel
+// select. Rows the mark kernel left to the multi-pass select, and rows of
+// at most topk positions, are done here as there.
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+topk_finish_kernel(const float* __restrict__ logits, int64_t logits_stride,
+                   const int32_t* __restrict__ lengths, int topk,
+                   int max_seqlen_k, uint32_t* __restrict__ key_hist,
+                   const uint32_t* __restrict__ ws, int64_t ws_row, int mw,
+                   const int32_t* __restrict__ table, int64_t table_stride,
+                   int64_t table_rows, const int32_t* __restrict__ t2r,
+                   int32_t* __restrict__ out, int64_t out_stride) {
+  __shared__ uint32_t hist[2048];   // multi-pass digits (<= 2048 bins)
+  __shared__ uint32_t bitmap[kMapWords];
+  __shared__ uint32_t cand_key[kCap];
+  __shared__ int32_t cand_pos[kCap];
+  __shared__ int scan_buf[2 * kWaves + 1];
+  __shared__ uint32_t s_sel[4];
+
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  // the row's threshold and both bitmaps are loaded before its length is
+  // known (words past the row's end are masked once it is; rows that need
+  // none of them ignore them), so these loads overlap the others
+  const uint32_t* prow = ws + t * ws_row;
+  const uint4 par = *reinterpret_cast<const uint4*>(prow);
+  const uint4* amap4 = reinterpret_cast<const uint4*>(prow + kSplitParams);
+  const uint4* bmap4 = reinterpret_cast<const uint4*>(prow + kSplitParams + mw);
+  // thread tid owns words 8 tid .. 8 tid + 7 of both bitmaps (mw and the
+  // row stride are multiples of 4 words, so the 16-byte loads stay in the
+  // row's mw words)
+  static_assert(kMapWords == 8 * kThreads, "8 bitmap words per thread");
+  uint32_t a[8], b[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int w = 8 * tid + 4 * h;
+    uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+    if (w < mw) { xa = amap4[w >> 2]; xb = bmap4[w >> 2]; }
+    a[4 * h] = xa.x; a[4 * h + 1] = xa.y; a[4 * h + 2] = xa.z; a[4 * h + 3] = xa.w;
+    b[4 * h] = xb.x; b[4 * h + 1] = xb.y; b[4 * h + 2] = xb.z; b[4 * h + 3] = xb.w;
+  }
+  int n = lengths[t];
+  n = n < 0 ? 0 : (n > max_seqlen_k ? max_seqlen_k : n);
+  int32_t* orow = out + t * out_stride;
+  static_assert(kThreads * 4 == kKeyBins, "one uint4 of key_hist per thread");
+  // every mark block of the row has read it (stream order)
+  reinterpret_cast<uint4*>(key_hist + t * kKeyBins)[tid] = make_uint4(0, 0, 0, 0);
+  const int32_t req = table ? t2r[t] : 0;
+  if (table && (req < 0 || req >= table_rows)) {
+    if (tid == 0) flag_device_error(NSA_DEVERR_REQUEST);
+    for (int j = tid; j < topk; j += kThreads) orow[j] = -1;
+    return;
+  }
+  const int32_t* trow = table ? table + (int64_t)req * table_stride : nullptr;
+  auto map = [&](int i) -> int32_t {
+    return trow ? (trow[i >> 6] << 6) + (i & 63) : i;
+  };
+  if (n <= topk) {
+    for (int j = tid; j < topk; j += kThreads) orow[j] = j < n ? map(j) : -1;
+    return;
+  }
+  const float* row = logits + t * logits_stride;
+  if (par.x != 0) {
+    select_multipass(row, n, VEC, topk, orow, map, hist, scan_buf, s_sel);
+    return;
+  }
+  const uint32_t bin = par.y;
+  const int krem = (int)par.z;
+  const bool exact = par.w != 0;
+  // words at or past nw (<= kMapWords: longer rows take the multi-pass
+  // select) were never written and count as zero
+  const int nw = (n + 31) >> 5;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (8 * tid + i >= nw) { a[i] = 0u; b[i] = 0u; }
+    cnt += __popc(b[i]);
+  }
+  if (8 * tid < nw) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      reinterpret_cast<uint4*>(bitmap)[2 * tid + h] =
+          make_uint4(a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]);
+  }
+  int ncand;
+  int q = block_exclusive_scan(cnt, scan_buf, &ncand);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t bits = b[i];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (q < kCap) cand_pos[q] = (8 * tid + i) * 32 + bit;
+      ++q;
+    }
   }
   __syncthreads();
-  int32_t* ptab = reinterpret_cast<int32_t*>(cand_key);   // >= 4096 entries
-  static_assert(kCP >= kTabPer * kThreads, "page table fits the candidate store");
-  if (trow) {
-#pragma unroll
-    for (int k = 0; k < kTabPer; ++k) ptab[tid + k * kThreads] = tab[k];
-  }
-
-  // ---- kept positions in ascending order: each thread owns a run of words
-  // (the scan's barriers also publish the page table)
-  const int per = (nw + kThreads - 1) / kThreads;
-  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
-  int cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
-  int kept;
-  int o = block_exclusive_scan(cnt, scan_buf, &kept);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = bitmap[w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int i = w * 32 + b;
-      if (o < topk) orow[o] = trow ? (ptab[i >> 6] << 6) + (i & 63) : i;
-      ++o;
-    }
-  }
+  finish_select<kCap>(row, n, topk, bin, krem, exact, min(ncand, kCap), trow,
+                      lengths, hist, bitmap, cand_key, cand_pos, scan_buf, s_sel,
+                      orow);
 }
 
 }  // namespace
@@ -693,13 +951,39 @@ extern "C" int nsa_topk_transform(const float* logits, int64_t logits_stride,
   return nsa::check_launch(fn);
 }
 
+// Rows split over mark blocks: only for rows longer than a segment that fit
+// the bitmaps, and for at most kSplitMaxRows rows. The one-kernel select runs
+// one block per row, so with at most half as many rows as the 256 CUs of an
+// MI355X most CUs idle and a long row's pass over its logits bounds it; with
+// more rows it already uses every CU, and the finish launch's fixed cost
+// (about 60% of the one-kernel time at 256 rows) makes the split slower.
+constexpr int kSplitMaxRows = 128;
+static bool split_select(int T, int max_seqlen_k, int topk) {
+  return T <= kSplitMaxRows && max_seqlen_k > topk && max_seqlen_k > kSeg &&
+         max_seqlen_k <= kMapBits;
+}
+
+extern "C" int nsa_topk_hist_workspace_size(int T, int max_seqlen_k, int topk,
+                                            size_t* bytes) {
+  NSA_REQUIRE(bytes != nullptr, NSA_ERR_INVALID_ARG,
+              "nsa_topk_hist_workspace_size: null output");
+  NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0 && topk >= 0, NSA_ERR_INVALID_ARG,
+              "nsa_topk_hist_workspace_size: negative size");
+  *bytes = T > 0 && split_select(T, max_seqlen_k, topk)
+               ? (size_t)T * (kSplitParams + 2 * (size_t)split_map_words(max_seqlen_k)) *
+                     sizeof(uint32_t)
+               : 0;
+  return nsa::ok();
+}
+
 extern "C" int nsa_topk_transform_hist(const float* logits, int64_t logits_stride,
                                        const int32_t* lengths, int T, int topk,
                                        int max_seqlen_k, const int32_t* table,
                                        int64_t table_stride, int64_t table_rows,
                                        const int32_t* token_to_req, int page_size,
                                        uint32_t* key_hist, int32_t* out,
-                                       int64_t out_stride, void* stream) {
+                                       int64_t out_stride, void* workspace,
+                                       size_t ws_bytes, void* stream) {
   const char* fn = "nsa_topk_transform_hist";
   NSA_REQUIRE(T >= 0 && max_seqlen_k >= 0, NSA_ERR_INVALID_ARG,
               "%s: negative size", fn);
@@ -723,11 +1007,39 @@ extern "C" int nsa_topk_transform_hist(const float* logits, int64_t logits_strid
                 "%s: table_stride < ceil(max_seqlen_k/64)", fn);
     NSA_REQUIRE(table_rows >= 0, NSA_ERR_INVALID_ARG, "%s: negative table_rows", fn);
   }
+  size_t need = 0;
+  nsa_topk_hist_workspace_size(T, max_seqlen_k, topk, &need);
+  if (workspace != nullptr && need > 0) {
+    NSA_REQUIRE(ws_bytes >= need, NSA_ERR_WORKSPACE,
+                "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+    NSA_REQUIRE(nsa::aligned(workspace, 16), NSA_ERR_INVALID_ARG,
+                "%s: workspace must be 16-byte aligned", fn);
+  }
   const bool vec = logits && nsa::aligned(logits, 16) && logits_stride % 4 == 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (workspace != nullptr && need > 0) {
+    const int segs = (max_seqlen_k + kSeg - 1) / kSeg;
+    const int mw = split_map_words(max_seqlen_k);
+    const int64_t ws_row = kSplitParams + 2 * (int64_t)mw;
+    const int64_t mark_blocks = ((int64_t)T + 7) / 8 * 8 * segs;
+    NSA_REQUIRE(mark_blocks < (1ll << 31), NSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    uint32_t* w = static_cast<uint32_t*>(workspace);
+    hipLaunchKernelGGL(vec ? topk_mark_kernel<true> : topk_mark_kernel<false>,
+                       dim3((unsigned)mark_blocks), dim3(kSegThreads), 0, s, logits,
+                       logits_stride, lengths, (int64_t)T, topk, max_seqlen_k, segs,
+                       key_hist, w, ws_row, mw);
+    int st = nsa::check_launch(fn);
+    if (st != NSA_OK) return st;
+    hipLaunchKernelGGL(vec ? topk_finish_kernel<true> : topk_finish_kernel<false>,
+                       dim3(T), dim3(kThreads), 0, s, logits, logits_stride, lengths,
+                       topk, max_seqlen_k, key_hist, w, ws_row, mw, table,
+                       table_stride, table_rows, token_to_req, out, out_stride);
+    return nsa::check_launch(fn);
+  }
   const bool small = max_seqlen_k <= kSmallMapBits && T >= kSmallMinRows;
   auto sel = vec ? (small ? topk_select_kernel<true, true, true> : topk_select_kernel<true, true, false>)
                  : (small ? topk_select_kernel<false, true, true> : topk_select_kernel<false, true, false>);
-  hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(sel, dim3(T), dim3(kThreads), 0, s,
                      logits, logits_stride, lengths, topk, max_seqlen_k, 0,
                      nullptr, key_hist, table, table_stride, table_rows,
                      token_to_req, out, out_stride);

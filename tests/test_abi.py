@@ -182,7 +182,26 @@ def test_fused_histogram_entry_points_validate(lib):
                                        P(16), 1, 4, 64, 64, 256, P(16), 256, P(16), 1, N) == -2
     # misaligned key_hist for the top-k
     assert lib.nsa_topk_transform_hist(P(16), 256, P(16), 1, 64, 256, N, 0, 4, N, 64,
-                                       P(18), P(16), 64, N) == -1
+                                       P(18), P(16), 64, N, 0, N) == -1
+    assert "aligned" in _err(lib)
+    # the split select's workspace: sized per row when rows exceed one
+    # 16384-position segment, else 0; a given workspace too small is refused
+    ws = ctypes.c_size_t(99)
+    assert lib.nsa_topk_hist_workspace_size(4, 16384, 2048, ctypes.byref(ws)) == 0
+    assert ws.value == 0
+    assert lib.nsa_topk_hist_workspace_size(4, 16385, 2048, ctypes.byref(ws)) == 0
+    assert ws.value == 4 * (16 + 2 * 516) * 4
+    assert lib.nsa_topk_hist_workspace_size(4, 262145, 2048, ctypes.byref(ws)) == 0
+    assert ws.value == 0
+    assert lib.nsa_topk_hist_workspace_size(128, 65536, 2048, ctypes.byref(ws)) == 0
+    assert ws.value == 128 * (16 + 2 * 2048) * 4
+    assert lib.nsa_topk_hist_workspace_size(129, 65536, 2048, ctypes.byref(ws)) == 0
+    assert ws.value == 0            # more rows: one block per row fills the GPU
+    assert lib.nsa_topk_hist_workspace_size(-1, 65536, 2048, ctypes.byref(ws)) == -1
+    assert lib.nsa_topk_transform_hist(P(16), 131072, P(16), 4, 2048, 131072, N, 0, 4, N,
+                                       64, P(16), P(16), 2048, P(16), 4096, N) == -3
+    assert lib.nsa_topk_transform_hist(P(16), 131072, P(16), 4, 2048, 131072, N, 0, 4, N,
+                                       64, P(16), P(16), 2048, P(20), 1 << 22, N) == -1
     assert "aligned" in _err(lib)
 
 
@@ -222,7 +241,8 @@ def test_empty_batches_launch_nothing(lib):
     assert lib.nsa_indexer_logits_hist(N, 2, N, N, 2, 10, N, 4, 4, N, N, 0, 64, 128, 64,
                                        256, N, 256, N, 1, N) == 0
     assert lib.nsa_topk_transform(N, 0, N, 0, 64, 256, N, 0, 4, N, 64, N, 64, N, 0, N) == 0
-    assert lib.nsa_topk_transform_hist(N, 0, N, 0, 64, 256, N, 0, 4, N, 64, N, N, 64, N) == 0
+    assert lib.nsa_topk_transform_hist(N, 0, N, 0, 64, 256, N, 0, 4, N, 64, N, N, 64, N,
+                                       0, N) == 0
     assert lib.nsa_page_table_transform(N, 64, 0, 64, N, 0, 0, P(16), 4, 4, 4, 64, N, N,
                                         64, N) == 0
     for entry in (lib.nsa_sparse_mla_decode, lib.nsa_sparse_mla_extend):

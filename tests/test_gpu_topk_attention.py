@@ -97,14 +97,16 @@ def test_topk_exact_on_given_logits(kind, topk, pad, span):
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("pad", [6, 67])
-@pytest.mark.parametrize("span", ["long", "short"])
-def test_topk_with_histogram_exact_on_given_logits(kind, pad, span):
+@pytest.mark.parametrize("span,split", [("long", True), ("long", False), ("short", True)])
+def test_topk_with_histogram_exact_on_given_logits(kind, pad, span, split):
     # the select that takes the indexer's row histograms (here the histogram
     # of the same logits, computed on the host from its definition): each
-    # row equals the oracle's set, and the histogram is left zero
+    # row equals the oracle's set, and the histogram is left zero. "long"
+    # rows run both the split select (rows over 16384 positions classified
+    # by many blocks, through a workspace) and the one-block-per-row select
     nsa = need_gpu()
     topk = 2048
-    note(f"topk with histogram {kind} pad={pad} {span}")
+    note(f"topk with histogram {kind} pad={pad} {span} split={split}")
     rng = np.random.default_rng(7)
     lengths = LENGTHS[span](topk)
     n0 = len(lengths)
@@ -116,7 +118,8 @@ def test_topk_with_histogram_exact_on_given_logits(kind, pad, span):
     kh = torch.as_tensor(kh_host.astype(np.uint32).view(np.int32), device=DEV)
     lg = torch.as_tensor(xt, device=DEV)
     ln = torch.as_tensor(lt, dtype=torch.int32, device=DEV)
-    got = nsa.nsa_topk_transform(lg, ln, topk, width, key_hist=kh).cpu().numpy()
+    got = nsa.nsa_topk_transform(lg, ln, topk, width, key_hist=kh,
+                                 split=split).cpu().numpy()
     assert int(kh.abs().sum()) == 0
     _check_repeats(got, n0)
     for t, L in enumerate(lengths):
@@ -125,6 +128,54 @@ def test_topk_with_histogram_exact_on_given_logits(kind, pad, span):
         want = oracle.topk.topk_row(x[t].astype(np.float64), L, topk)
         want = np.sort(want[want >= 0])
         np.testing.assert_array_equal(sel[:len(want)], want, err_msg=f"row {t} L={L}")
+
+
+@pytest.mark.parametrize("pad", [0, 67])   # vector loads; odd stride: scalar loads
+def test_topk_split_select_matches_one_block_select(pad):
+    # rows around the 16384-position segments of the split select (1..3
+    # positions past a segment's or the row's last whole vector, rows of at
+    # most topk, one row whose histogram does not add up to its length: the
+    # multi-pass select), mapped through a page table: the split select and
+    # the one-block-per-row select give identical slots, equal to the
+    # oracle's, also on a second call over a workspace that still holds the
+    # first call's bitmaps (and starts as garbage)
+    nsa = need_gpu()
+    topk = 2048
+    note(f"topk split vs one-block pad={pad}")
+    rng = np.random.default_rng(11 + pad)
+    lengths = [0, 2048, 2049, 16383, 16384, 16385, 16387, 32769, 49151, 65535,
+               100002, 131071, 131072]
+    T = len(lengths)
+    width = max(lengths) + pad
+    ncol = -(-width // 64)
+    table_h = rng.permutation(3 * ncol)[:2 * ncol].reshape(2, ncol)
+    table = torch.as_tensor(table_h, dtype=torch.int32, device=DEV)
+    t2r_h = [t % 2 for t in range(T)]
+    t2r = torch.as_tensor(t2r_h, dtype=torch.int32, device=DEV)
+    ln = torch.as_tensor(lengths, dtype=torch.int32, device=DEV)
+    need = nsa.topk_hist_workspace_size(T, width, topk)
+    assert need > 0
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    for call in range(2):
+        x = _topk_rows(rng, lengths, width, "normal" if call == 0 else "special")
+        kh_host = np.stack([host_key_hist(x[t], L) for t, L in enumerate(lengths)])
+        kh_host[7, 4000] += 1                     # row 7: counts do not add up
+        lg = torch.as_tensor(x, device=DEV)
+        outs = []
+        for split in (True, False):
+            kh = torch.as_tensor(kh_host.astype(np.uint32).view(np.int32), device=DEV)
+            outs.append(nsa.nsa_topk_transform(
+                lg, ln, topk, width, table=table, token_to_req=t2r, key_hist=kh,
+                workspace=ws if split else None, split=split).cpu().numpy())
+            assert int(kh.abs().sum()) == 0
+        np.testing.assert_array_equal(outs[0], outs[1], err_msg=f"call {call}")
+        want = np.full((T, topk), -1, np.int64)
+        for t, L in enumerate(lengths):
+            w = oracle.topk.topk_row(x[t].astype(np.float64), L, topk)
+            w = np.sort(w[w >= 0])
+            want[t, :len(w)] = w
+        want = oracle.transform.transform_compact(want, table_h, t2r_h)
+        np.testing.assert_array_equal(outs[0], want, err_msg=f"call {call}")
 
 
 def test_topk_without_logits_when_rows_fit():
