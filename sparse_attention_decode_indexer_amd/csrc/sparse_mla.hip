@@ -905,7 +905,9 @@ template <int NS>
 __global__ void __launch_bounds__(256)
 combine_bf16_kernel(const uint16_t* __restrict__ ws_o, const float* __restrict__ ws_lse,
                     int T, int H, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // (row, head) pairs in XCD-contiguous order: the attention blocks of a
+  // row (and their partials, still in that XCD's L2) run on the same XCD
+  const int64_t th = (int64_t)xcd_logical_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   if (th >= (int64_t)T * H) return;
   const int lane = threadIdx.x & 63;
   const int64_t TH = (int64_t)T * H;
