@@ -25,6 +25,10 @@ def make_step(nsa, w, hint=1):
     logits = torch.empty(T, nsa.logits_row_stride(w.max_seqlen_k),
                          dtype=torch.float32, device=DEV)
     kh = nsa.new_key_hist(T, DEV)
+    # the split top-k's bitmaps (batches of at most 128 rows longer than one
+    # 16384-position segment: the reduced verify cases below)
+    tk_ws = torch.empty(max(nsa.topk_hist_workspace_size(T, w.max_seqlen_k, w.topk), 16),
+                        dtype=torch.uint8, device=DEV)
     slots = torch.empty(T, w.topk, dtype=torch.int32, device=DEV)
     if w.kv_kind == "fp8":
         cache, kvd = nsa.nsa_quantize_k_cache(w.kv_bf16), nsa.KV_FP8_656
@@ -50,7 +54,7 @@ def make_step(nsa, w, hint=1):
         nsa.nsa_topk_transform(logits, md["seqlens_expanded"], w.topk,
                                w.max_seqlen_k, table=md["real_page_table"],
                                token_to_req=md["token_to_req"], out=slots,
-                               key_hist=kh)
+                               key_hist=kh, workspace=tk_ws)
         attn(w.q, cache, kvd, slots, w.sm_scale, md["nsa_cache_seqlens"],
              out=out, lse=lse, workspace=ws)
 
@@ -91,7 +95,8 @@ def assert_same(got, want, what):
 def test_step_graph_replays_match_eager_and_oracle(name, overrides, hint):
     nsa = need_gpu()
     w = W.make_workload(name, device=DEV, **overrides)
-    note(f"graph: {name} T={w.num_rows} H={w.heads} kv={w.kv_kind} hint={hint}")
+    note(f"graph: {name} T={w.num_rows} H={w.heads} kv={w.kv_kind} hint={hint} "
+         f"split top-k={nsa.topk_hist_workspace_size(w.num_rows, w.max_seqlen_k, w.topk) > 0}")
     step, snapshot, scribble, against_oracle = make_step(nsa, w, hint)
     step()
     torch.cuda.synchronize()
