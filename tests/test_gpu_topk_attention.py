@@ -137,8 +137,10 @@ def test_topk_split_select_matches_one_block_select(pad):
     # most topk, one row whose histogram does not add up to its length: the
     # multi-pass select), mapped through a page table: the split select and
     # the one-block-per-row select give identical slots, equal to the
-    # oracle's, also on a second call over a workspace that still holds the
-    # first call's bitmaps (and starts as garbage)
+    # oracle's, also on later calls over a workspace that still holds the
+    # previous call's bitmaps (and starts as garbage). The third call packs
+    # 3000 keys of one threshold bin ([5, 5.5), many equal) into the first
+    # segment of every row: a crowded bin, resolved among ties by position
     nsa = need_gpu()
     topk = 2048
     note(f"topk split vs one-block pad={pad}")
@@ -156,8 +158,14 @@ def test_topk_split_select_matches_one_block_select(pad):
     need = nsa.topk_hist_workspace_size(T, width, topk)
     assert need > 0
     ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
-    for call in range(2):
-        x = _topk_rows(rng, lengths, width, "normal" if call == 0 else "special")
+    for call in range(3):
+        x = _topk_rows(rng, lengths, width, ["normal", "special", "normal"][call])
+        if call == 2:
+            for t, L in enumerate(lengths):
+                if L > 3100:
+                    x[t, :L] = np.clip(rng.normal(size=L) * 0.5, -3.9, 3.9)
+                    c = 5.0 + rng.integers(0, 400, size=3000) / 800.0
+                    x[t, 100:3100] = c.astype(np.float32)
         kh_host = np.stack([host_key_hist(x[t], L) for t, L in enumerate(lengths)])
         kh_host[7, 4000] += 1                     # row 7: counts do not add up
         lg = torch.as_tensor(x, device=DEV)
