@@ -116,13 +116,18 @@ def test_pipeline_full_size_spread_rows(name):
 
 
 @pytest.mark.parametrize("name,grouped", [("decode_b32", False), ("verify", False),
-                                          ("verify", True), ("extend", True)])
+                                          ("verify", True), ("extend", True),
+                                          ("decode_b128", False)])
 def test_fused_histogram_exact_and_topk_identical(name, grouped):
     # grouped: the rows-per-request hint of the workload, which scores a
-    # request's rows four at a time (verify: its 4 drafts; extend)
+    # request's rows four at a time (verify: its 4 drafts; extend).
+    # decode_b128 (128 rows of up to 131072 positions) runs the split select
+    # (mark and finish kernels) with the binding's workspace; the others run
+    # one block per row
     nsa = need_gpu()
     w = full_workload(name)
-    note(f"fused histogram {name}: T={w.num_rows} grouped={grouped}")
+    note(f"fused histogram {name}: T={w.num_rows} grouped={grouped} split top-k="
+         f"{nsa.topk_hist_workspace_size(w.num_rows, w.max_seqlen_k, w.topk) > 0}")
     md = gpu_metadata(nsa, w)
     kh = nsa.new_key_hist(w.num_rows, DEV)
     logits = nsa.nsa_indexer_logits(w.q_idx, w.idx_weights, w.index_cache,
